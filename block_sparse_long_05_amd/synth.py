@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for the MSA hot path.
+
+This module only draws data. It holds no step of the method (no scoring, pooling,
+selection or attention), so both the CPU oracle and the HIP path can take their
+inputs from it without sharing any of the method's arithmetic.
+
+Shapes follow the workloads of the MiniMax Sparse Attention pages (researchpapers.dev
+summary, "Key results": 16 blocks x 128 tokens per query group; mlqm.cn blog, section 2.1:
+one index query per GQA group and one shared index-key head):
+
+prefill
+    q      [T, G*Hpg, D]     query heads, head h belongs to group h // Hpg
+    k, v   [G, T, D]         one K/V head per GQA group
+    q_idx  [T, G, d_idx]     one index query per token and group
+    k_idx  [T, d_idx]        the single shared index-key head
+decode
+    q       [B, G*Hpg, D]
+    k_cache [B, G, Lmax, D], v_cache likewise
+    q_idx   [B, G, d_idx]
+    k_idx   [B, Lmax, d_idx]
+    seq_lens [B] int32 (cache length per sequence, the current token included)
+
+Values are i.i.d. N(0, 1) drawn in fp32 from a seeded torch generator and, for bf16
+workloads, rounded once to bf16 (round to nearest even). Both sides consume exactly
+the same rounded tensors.
+
+Planted blocks make the index branch's choice clear-cut on part of the rows:
+prefill: per group a direction u_g ~ N(0, I) is added to every index query of that
+    group, and 4*u_g to the index keys of `planted_per_group` random whole blocks.
+decode: per (sequence, group) `planted_per_group` random blocks get 4*q_idx[b, g]
+    added to their index keys.
+"""
+
+from __future__ import annotations
+
+import torch
+
+BLOCK = 128
+_CHUNK_ROWS = 1 << 16
+
+
+def _dtype(name: str) -> torch.dtype:
+    if name in ("bf16", "bfloat16"):
+        return torch.bfloat16
+    if name in ("f32", "fp32", "float32"):
+        return torch.float32
+    raise ValueError(f"unknown dtype {name!r}")
+
+
+def _gen(device, seed: int, tensor_id: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + tensor_id * 7919) & ((1 << 62) - 1))
+    return g
+
+
+def _randn_into(out: torch.Tensor, gen: torch.Generator) -> torch.Tensor:
+    """Fill `out` with N(0,1) drawn in fp32, chunked along dim 0 to bound temporaries."""
+    flat = out.view(out.shape[0], -1)
+    rows_per = max(1, (_CHUNK_ROWS * 128) // max(1, flat.shape[1]))
+    for r0 in range(0, flat.shape[0], rows_per):
+        r1 = min(flat.shape[0], r0 + rows_per)
+        tmp = torch.randn((r1 - r0, flat.shape[1]), generator=gen, device=out.device,
+                          dtype=torch.float32)
+        flat[r0:r1].copy_(tmp)
+    return out
+
+
+def _randn(shape, dtype, device, gen):
+    return _randn_into(torch.empty(shape, dtype=dtype, device=device), gen)
+
+
+def _distinct_blocks(n_pick: int, n_blocks: int, gen: torch.Generator, device) -> torch.Tensor:
+    n_pick = min(n_pick, n_blocks)
+    perm = torch.randperm(n_blocks, generator=gen, device=device)
+    return perm[:n_pick].to("cpu")
+
+
+def prefill_inputs(T: int, G: int, Hpg: int, D: int = 128, d_idx: int = 128,
+                   dtype: str = "bf16", seed: int = 0, planted_per_group: int = 0,
+                   plant_scale: float = 4.0, device="cpu") -> dict:
+    """Inputs of one causal prefill over T tokens (see module docstring)."""
+    dt = _dtype(dtype)
+    dev = torch.device(device)
+    q = _randn((T, G * Hpg, D), dt, dev, _gen(dev, seed, 1))
+    k = _randn((G, T, D), dt, dev, _gen(dev, seed, 2))
+    v = _randn((G, T, D), dt, dev, _gen(dev, seed, 3))
+    planted = torch.empty((G, 0), dtype=torch.int64)
+    n_full = T // BLOCK
+    if planted_per_group > 0 and n_full > 0:
+        gen_p = _gen(dev, seed, 6)
+        u = torch.randn((G, d_idx), generator=gen_p, device=dev, dtype=torch.float32)
+        q_idx = torch.empty((T, G, d_idx), dtype=dt, device=dev)
+        gq = _gen(dev, seed, 4)
+        for t0 in range(0, T, _CHUNK_ROWS):
+            t1 = min(T, t0 + _CHUNK_ROWS)
+            z = torch.randn((t1 - t0, G, d_idx), generator=gq, device=dev, dtype=torch.float32)
+            q_idx[t0:t1].copy_(z + u[None])
+        k_idx32 = torch.empty((T, d_idx), dtype=torch.float32, device=dev)
+        _randn_into(k_idx32, _gen(dev, seed, 5))
+        rows = []
+        for g in range(G):
+            blocks = _distinct_blocks(planted_per_group, n_full, gen_p, dev)
+            rows.append(blocks)
+            for c in blocks.tolist():
+                k_idx32[c * BLOCK:(c + 1) * BLOCK] += plant_scale * u[g]
+        planted = torch.stack(rows)
+        k_idx = k_idx32.to(dt)
+        del k_idx32
+    else:
+        q_idx = _randn((T, G, d_idx), dt, dev, _gen(dev, seed, 4))
+        k_idx = _randn((T, d_idx), dt, dev, _gen(dev, seed, 5))
+    return dict(q=q, k=k, v=v, q_idx=q_idx, k_idx=k_idx, planted=planted)
+
+
+def decode_inputs(B: int, max_len: int, G: int, Hpg: int, D: int = 128, d_idx: int = 128,
+                  dtype: str = "bf16", seed: int = 0, planted_per_group: int = 0,
+                  plant_scale: float = 4.0, seq_lens=None, device="cpu") -> dict:
+    """Inputs of one decode step of B sequences against a KV cache of capacity max_len.
+
+    seq_lens defaults to max_len for every sequence; a list gives ragged lengths.
+    """
+    dt = _dtype(dtype)
+    dev = torch.device(device)
+    if seq_lens is None:
+        seq_lens = [max_len] * B
+    seq_lens = [int(x) for x in seq_lens]
+    if len(seq_lens) != B or min(seq_lens) < 1 or max(seq_lens) > max_len:
+        raise ValueError("seq_lens must hold B lengths in [1, max_len]")
+    q = _randn((B, G * Hpg, D), dt, dev, _gen(dev, seed, 11))
+    k_cache = torch.empty((B, G, max_len, D), dtype=dt, device=dev)
+    v_cache = torch.empty((B, G, max_len, D), dtype=dt, device=dev)
+    gk, gv = _gen(dev, seed, 12), _gen(dev, seed, 13)
+    for b in range(B):
+        for g in range(G):
+            _randn_into(k_cache[b, g], gk)
+            _randn_into(v_cache[b, g], gv)
+    q_idx = _randn((B, G, d_idx), dt, dev, _gen(dev, seed, 14))
+    k_idx = torch.empty((B, max_len, d_idx), dtype=dt, device=dev)
+    gki = _gen(dev, seed, 15)
+    planted = torch.empty((B, G, 0), dtype=torch.int64)
+    if planted_per_group > 0:
+        gen_p = _gen(dev, seed, 16)
+        q_idx32 = q_idx.to(torch.float32)
+        per_b = []
+        for b in range(B):
+            kb = torch.empty((max_len, d_idx), dtype=torch.float32, device=dev)
+            _randn_into(kb, gki)
+            n_blk = (seq_lens[b] + BLOCK - 1) // BLOCK
+            per_g = []
+            for g in range(G):
+                blocks = _distinct_blocks(planted_per_group, n_blk, gen_p, dev)
+                per_g.append(blocks)
+                for c in blocks.tolist():
+                    kb[c * BLOCK:min((c + 1) * BLOCK, max_len)] += plant_scale * q_idx32[b, g]
+            per_b.append(torch.stack(per_g))
+            k_idx[b].copy_(kb)
+            del kb
+        planted = torch.stack(per_b)
+    else:
+        for b in range(B):
+            _randn_into(k_idx[b], gki)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device=dev)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, q_idx=q_idx, k_idx=k_idx,
+                seq_lens=lens, planted=planted)

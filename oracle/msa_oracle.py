@@ -1,0 +1,267 @@
+"""Plain CPU oracle of the MiniMax Sparse Attention (MSA) hot path, in NumPy float64.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this module:
+only the test suite, the package smoke check and the benchmark's CPU-baseline leg use
+it. It shares no code, table or helper with the HIP kernels.
+
+What it computes, and where the pages say so:
+
+* Index branch (mlqm.cn blog on the MiniMax M3 sparse attention, section 2.1;
+  researchpapers.dev MSA summary, "Mechanism"): one index query per GQA group is
+  dotted with the single shared index-key head, s_j = Q_idx[t, g] . K_idx[j]; the
+  token scores are reduced to one score per 128-token block by max pooling; per
+  (query, group) the top-k blocks are kept and the most recent (local) block is
+  always kept. Only visible tokens are scored.
+* Main branch (same blog, section 2.2, the gather + flash-attention pseudo-code;
+  researchpapers.dev summary, "Mechanism": exact softmax attention on the selected
+  blocks): every query head of the group attends, with exact softmax, to the keys of
+  the selected blocks that are causally visible, O = softmax(q K^T / sqrt(d)) V
+  (the scaled dot-product formula of the Lightning-attention explainer, section 2.1).
+* Budget: 16 blocks of 128 tokens per query group (researchpapers.dev summary,
+  "2048 KV tokens").
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  R1 index score = raw dot product, no scale (any positive scale keeps the ranking);
+  R2 block c covers tokens [128c, 128c + 127];
+  R3 causal: query t sees j <= t; local block b = t // 128; blocks > b are never chosen;
+  R4 top_k counts the local block: Sel = {b} + the (top_k - 1) best of blocks [0, b);
+  R5 when b + 1 <= top_k every visible block is selected;
+  R6 ranking: higher block score first, then lower block index (-0.0 == +0.0);
+  R7 near tie: last selected vs first unselected non-local score, relative gap < 1e-5;
+  R8 head h belongs to group h // Hpg;
+  R9 attention scale 1 / sqrt(head_dim);
+  R11 decode: a cache of L tokens holds the current token, whose position is L - 1.
+
+The inputs may be NumPy arrays or torch tensors (fp32 / bf16); they are widened
+exactly to float64 first.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 128
+NEAR_TIE_REL = 1e-5
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact widening of fp32 / bf16 / fp64 data (NumPy or torch) to float64."""
+    if hasattr(x, "detach"):  # torch tensor; bf16 -> fp32 is exact
+        import torch
+        x = x.detach().to("cpu")
+        if x.dtype != torch.float64:
+            x = x.to(torch.float32)
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------------
+# Index branch
+# ----------------------------------------------------------------------------------
+
+def index_block_scores(q_idx_rows: np.ndarray, k_idx: np.ndarray, b: int,
+                       block: int = BLOCK) -> np.ndarray:
+    """Block scores of blocks 0..b-1 for index-query rows that share local block b.
+
+    q_idx_rows [R, d_idx]; k_idx [>= b*block, d_idx]. Token scores are the matrix
+    product Q_idx . K_idx^T over the keys of the fully visible blocks (blog section
+    2.1), and a block's score is the max over its 128 token scores (block max
+    pooling, same section). Returns [R, b].
+    """
+    keys = k_idx[: b * block]
+    s = q_idx_rows @ keys.T                      # [R, b*block] token scores
+    return s.reshape(s.shape[0], b, block).max(axis=2)
+
+
+def select_blocks(block_scores: np.ndarray, b: int, top_k: int):
+    """Blocks kept for one (query, group) row whose local block is b.
+
+    block_scores holds the scores of blocks 0..b-1 (the local block is not scored:
+    it is always kept, researchpapers.dev summary, "Mechanism"). Returns
+    (ascending block ids, near_tie flag).
+    """
+    if b + 1 <= top_k:                           # R5: everything visible fits
+        return np.arange(b + 1, dtype=np.int64), False
+    scores = np.asarray(block_scores, dtype=np.float64)[:b] + 0.0   # -0.0 -> +0.0
+    # R6: sort by score descending, then block index ascending.
+    order = np.lexsort((np.arange(b), -scores))
+    chosen = order[: top_k - 1]
+    sel = np.sort(np.concatenate([chosen, [b]])).astype(np.int64)
+    tie = False
+    if top_k >= 2:
+        hi = scores[order[top_k - 2]]            # last selected non-local score
+        lo = scores[order[top_k - 1]]            # first unselected score
+        den = max(abs(hi), abs(lo))
+        tie = True if den == 0.0 else bool((hi - lo) / den < NEAR_TIE_REL)
+    return sel, tie
+
+
+# ----------------------------------------------------------------------------------
+# Main branch
+# ----------------------------------------------------------------------------------
+
+def attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray,
+           scale: float) -> np.ndarray:
+    """Exact softmax attention of q_heads [H, D] over keys/values [n, D]."""
+    logits = (q_heads @ keys.T) * scale
+    logits = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    return (p @ values) / p.sum(axis=1, keepdims=True)
+
+
+def visible_keys(sel, t: int, block: int = BLOCK) -> np.ndarray:
+    """Token ids of the selected blocks that query position t can see (j <= t)."""
+    parts = [np.arange(c * block, min(c * block + block, t + 1)) for c in sel]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def _row(q_t, k_g, v_g, q_idx_tg, k_idx, t, top_k, block, scale, bs=None):
+    b = t // block
+    if b + 1 <= top_k:
+        sel, tie = np.arange(b + 1, dtype=np.int64), False
+    else:
+        if bs is None:
+            bs = index_block_scores(q_idx_tg[None, :], k_idx, b, block)[0]
+        sel, tie = select_blocks(bs, b, top_k)
+    j = visible_keys(sel, t, block)
+    return attend(q_t, k_g[j], v_g[j], scale), sel, tie, bs
+
+
+def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) -> dict:
+    """Causal MSA prefill for the query positions `rows` (default: all).
+
+    q [T, G*Hpg, D]; k, v [G, T, D]; q_idx [T, G, d_idx]; k_idx [T, d_idx].
+    Returns dict(out [R, Hq, D], sel [R][G] -> ascending ids, near_tie [R, G] bool,
+    block_scores {(i, g): array of b scores} for rows that were scored, rows [R]).
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    q_idx, k_idx = as_f64(q_idx), as_f64(k_idx)
+    T, Hq, D = q.shape
+    G = k.shape[0]
+    Hpg = Hq // G
+    scale = 1.0 / math.sqrt(D)                   # R9
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), Hq, D))
+    sel_all = [[None] * G for _ in rows]
+    tie = np.zeros((len(rows), G), dtype=bool)
+    scores = {}
+    # Rows sharing a local block b see the same keys, so their block scores come
+    # from one matrix product Q_idx . K_idx^T.
+    by_block = {}
+    for i, t in enumerate(rows.tolist()):
+        by_block.setdefault(t // block, []).append(i)
+    for b, idxs in by_block.items():
+        bs_rows = None
+        if b + 1 > top_k:
+            qi = q_idx[rows[idxs]].reshape(len(idxs) * G, -1)
+            bs_rows = index_block_scores(qi, k_idx, b, block).reshape(len(idxs), G, b)
+        for n, i in enumerate(idxs):
+            t = int(rows[i])
+            for g in range(G):
+                hs = slice(g * Hpg, (g + 1) * Hpg)   # R8
+                bs = None if bs_rows is None else bs_rows[n, g]
+                o, sel, tg, bs = _row(q[t, hs], k[g], v[g], q_idx[t, g], k_idx, t, top_k,
+                                      block, scale, bs)
+                out[i, hs] = o
+                sel_all[i][g] = sel
+                tie[i, g] = tg
+                if bs is not None:
+                    scores[(i, g)] = bs
+    return dict(out=out, sel=sel_all, near_tie=tie, block_scores=scores, rows=rows)
+
+
+def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
+           block: int = BLOCK) -> dict:
+    """One MSA decode step for B sequences.
+
+    q [B, G*Hpg, D]; k_cache, v_cache [B, G, Lmax, D]; q_idx [B, G, d_idx];
+    k_idx [B, Lmax, d_idx]; seq_lens [B]. The query sits at position L_b - 1 (R11).
+    """
+    q, kc, vc = as_f64(q), as_f64(k_cache), as_f64(v_cache)
+    q_idx, k_idx = as_f64(q_idx), as_f64(k_idx)
+    lens = [int(x) for x in np.asarray(as_f64(seq_lens)).tolist()]
+    B, Hq, D = q.shape
+    G = kc.shape[1]
+    Hpg = Hq // G
+    scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    sel_all = [[None] * G for _ in range(B)]
+    tie = np.zeros((B, G), dtype=bool)
+    scores = {}
+    for bi in range(B):
+        t = lens[bi] - 1
+        for g in range(G):
+            hs = slice(g * Hpg, (g + 1) * Hpg)
+            o, sel, tg, bs = _row(q[bi, hs], kc[bi, g], vc[bi, g], q_idx[bi, g], k_idx[bi],
+                                  t, top_k, block, scale)
+            out[bi, hs] = o
+            sel_all[bi][g] = sel
+            tie[bi, g] = tg
+            if bs is not None:
+                scores[(bi, g)] = bs
+    return dict(out=out, sel=sel_all, near_tie=tie, block_scores=scores)
+
+
+# ----------------------------------------------------------------------------------
+# Dense GQA attention (the comparison baseline of the researchpapers.dev summary,
+# "Key results": MSA against dense GQA with the same heads)
+# ----------------------------------------------------------------------------------
+
+def dense_prefill(q, k, v, rows=None) -> np.ndarray:
+    """Causal softmax attention of every head over all keys j <= t of its group."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    T, Hq, D = q.shape
+    G = k.shape[0]
+    Hpg = Hq // G
+    scale = 1.0 / math.sqrt(D)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), Hq, D))
+    for i, t in enumerate(rows.tolist()):
+        for g in range(G):
+            hs = slice(g * Hpg, (g + 1) * Hpg)
+            out[i, hs] = attend(q[t, hs], k[g, : t + 1], v[g, : t + 1], scale)
+    return out
+
+
+def dense_decode(q, k_cache, v_cache, seq_lens) -> np.ndarray:
+    """Softmax attention of each sequence's query over its whole cache."""
+    q, kc, vc = as_f64(q), as_f64(k_cache), as_f64(v_cache)
+    lens = [int(x) for x in np.asarray(as_f64(seq_lens)).tolist()]
+    B, Hq, D = q.shape
+    G = kc.shape[1]
+    Hpg = Hq // G
+    scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    for bi in range(B):
+        L = lens[bi]
+        for g in range(G):
+            hs = slice(g * Hpg, (g + 1) * Hpg)
+            out[bi, hs] = attend(q[bi, hs], kc[bi, g, :L], vc[bi, g, :L], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Helpers for comparing against a device result
+# ----------------------------------------------------------------------------------
+
+def selection_array(sel, top_k: int) -> np.ndarray:
+    """Pack a [R][G] list of ascending id arrays as [R, G, top_k] int32, -1 padded."""
+    R, G = len(sel), len(sel[0])
+    a = np.full((R, G, top_k), -1, dtype=np.int32)
+    for i in range(R):
+        for g in range(G):
+            s = sel[i][g]
+            a[i, g, : len(s)] = s
+    return a
+
+
+def attend_on_selection(q_t, k_g, v_g, sel, t, block: int = BLOCK) -> np.ndarray:
+    """Attention of one token's group heads over a given selection (for rows where
+    a device picked a different set on a declared near tie)."""
+    q_t, k_g, v_g = as_f64(q_t), as_f64(k_g), as_f64(v_g)
+    sel = [int(c) for c in sel if int(c) >= 0]
+    j = visible_keys(sel, t, block)
+    return attend(q_t, k_g[j], v_g[j], 1.0 / math.sqrt(q_t.shape[-1]))

@@ -1,0 +1,218 @@
+"""Pins of the CPU oracle to facts outside itself (closed forms, library routines,
+hand-enumerated cases, brute force). CPU only.
+
+Each test names the mistake it is meant to catch.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as orc
+from block_sparse_long_05_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch's scaled_dot_product_attention in fp64 on the CPU.
+
+    q [T, Hq, D], k/v [G, T, D] -> [T, Hq, D]; enable_gqa maps head h to KV head
+    h // (Hq / G). mask: bool [Hq or 1, T, T], True = may attend.
+    """
+    qq = torch.as_tensor(orc.as_f64(q)).permute(1, 0, 2)[None]
+    kk = torch.as_tensor(orc.as_f64(k))[None]
+    vv = torch.as_tensor(orc.as_f64(v))[None]
+    m = None if mask is None else torch.as_tensor(mask)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=m, is_causal=causal, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _small(T=300, G=2, Hpg=3, D=32, d_idx=16, seed=1, planted=0):
+    return synth.prefill_inputs(T, G, Hpg, D, d_idx, dtype="f32", seed=seed,
+                                planted_per_group=planted)
+
+
+# -- Top-k rule: hand-enumerated cases --------------------------------------------
+
+def test_topk_hand_enumerated():
+    """Catches: wrong tie-break, local block not forced, k counting the local block
+    wrongly, -0.0 ordered below +0.0, near-tie threshold or direction."""
+    with open(os.path.join(GOLDEN, "topk_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        sel, tie = orc.select_blocks(np.array(c["scores"], dtype=np.float64), c["b"], c["top_k"])
+        assert sel.tolist() == c["expect"], c["name"]
+        assert tie == c["near_tie"], c["name"]
+
+
+# -- Index scores: brute force in pure Python on a tiny input ------------------------
+
+def test_block_scores_brute_force():
+    """Catches: mean instead of max pooling, a dropped or extra block, scoring the
+    local block, keys taken from the wrong rows, transposed operands."""
+    rng = np.random.default_rng(3)
+    blk, b, d = 4, 5, 3
+    k_idx = rng.standard_normal((blk * 7, d))
+    q_rows = rng.standard_normal((2, d))
+    got = orc.index_block_scores(q_rows, k_idx, b, block=blk)
+    assert got.shape == (2, b)
+    for r in range(2):
+        for c in range(b):
+            best = -math.inf
+            for j in range(c * blk, c * blk + blk):
+                s = 0.0
+                for e in range(d):
+                    s += float(q_rows[r, e]) * float(k_idx[j, e])
+                best = max(best, s)
+            assert abs(got[r, c] - best) < 1e-12
+
+
+# -- Dense equivalence: all blocks selected == causal GQA attention (library) -------
+
+@pytest.mark.parametrize("T,G,Hpg,D,d_idx", [(300, 2, 3, 32, 16), (257, 1, 4, 16, 8),
+                                              (130, 3, 2, 24, 24)])
+def test_dense_equivalence_library(T, G, Hpg, D, d_idx):
+    """k >= number of blocks: MSA equals dense causal GQA attention computed by
+    torch's SDPA (fp64). Catches: a missing or wrong 1/sqrt(head_dim) (d_idx !=
+    head_dim here), head->group mapping h % G instead of h // Hpg, causal off-by-one,
+    a dropped key of the ragged last block."""
+    x = _small(T, G, Hpg, D, d_idx, seed=T)
+    nblk = (T + 127) // 128
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=nblk)
+    ref = _sdpa(x["q"], x["k"], x["v"], causal=True)
+    assert np.max(np.abs(res["out"] - ref)) < 1e-12
+    assert np.max(np.abs(orc.dense_prefill(x["q"], x["k"], x["v"]) - ref)) < 1e-12
+
+
+def test_local_only_equals_block_diagonal_mask():
+    """top_k = 1: each query sees only its own block up to itself. Catches a local
+    block that includes future tokens or misses the block start."""
+    x = _small(T=400, G=2, Hpg=2, D=16, d_idx=8, seed=7)
+    T = 400
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=1)
+    t = np.arange(T)
+    mask = (t[None, :] <= t[:, None]) & (t[None, :] // 128 == t[:, None] // 128)
+    ref = _sdpa(x["q"], x["k"], x["v"], mask=mask[None])
+    assert np.max(np.abs(res["out"] - ref)) < 1e-12
+
+
+def test_sparse_equals_masked_attention():
+    """Given the oracle's selection, the output equals SDPA with a per-head mask that
+    admits exactly the selected, causally visible keys. Catches gathering the wrong
+    tokens for a block, using another group's selection, masking the partial block."""
+    T, G, Hpg = 700, 2, 3
+    x = _small(T=T, G=G, Hpg=Hpg, D=32, d_idx=16, seed=11)
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=3)
+    mask = np.zeros((G * Hpg, T, T), dtype=bool)
+    for t in range(T):
+        for g in range(G):
+            for c in res["sel"][t][g]:
+                lo, hi = c * 128, min(c * 128 + 128, t + 1)
+                mask[g * Hpg:(g + 1) * Hpg, t, lo:hi] = True
+    ref = _sdpa(x["q"], x["k"], x["v"], mask=mask)
+    assert np.max(np.abs(res["out"] - ref)) < 1e-12
+    assert any(len(res["sel"][t][0]) == 3 for t in range(T))
+
+
+# -- Selection invariants, brute force over every row --------------------------------
+
+def test_selection_invariants_every_row():
+    """|Sel| = min(k, b+1); the local block is in Sel; no future block; every
+    unselected visible block ranks below every selected non-local block in the order
+    (score desc, index asc), with scores recomputed by a separate brute-force loop."""
+    T, G, k = 1100, 2, 4
+    x = _small(T=T, G=G, Hpg=1, D=8, d_idx=6, seed=5)
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=k)
+    qi, ki = orc.as_f64(x["q_idx"]), orc.as_f64(x["k_idx"])
+    for t in range(T):
+        b = t // 128
+        for g in range(G):
+            sel = list(res["sel"][t][g])
+            assert len(sel) == min(k, b + 1)
+            assert b in sel and max(sel) == b and sel == sorted(sel)
+            if b + 1 <= k:
+                continue
+            s = [max(float(np.dot(qi[t, g], ki[j])) for j in range(c * 128, c * 128 + 128))
+                 for c in range(b)]
+            key = lambda c: (-s[c], c)
+            worst_sel = max((c for c in sel if c != b), key=key)
+            for c in range(b):
+                if c not in sel:
+                    assert key(c) > key(worst_sel)
+
+
+# -- Planted recovery ----------------------------------------------------------------
+
+def test_planted_blocks_are_selected():
+    """With 4*u_g planted into some blocks' index keys and u_g added to every index
+    query, visible planted blocks win the top-k (data-level check of scoring +
+    selection working together; catches a sign flip in the score)."""
+    T, G, k = 4096, 2, 6
+    x = synth.prefill_inputs(T, G, 1, 16, 32, dtype="f32", seed=9, planted_per_group=4)
+    rows = np.arange(128 * 20, T, 97)
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=k, rows=rows)
+    planted = x["planted"].numpy()
+    for i, t in enumerate(rows):
+        b = t // 128
+        for g in range(G):
+            vis = [c for c in planted[g] if c < b]
+            assert set(vis) <= set(res["sel"][i][g].tolist())
+
+
+# -- Decode equals the last prefill row ---------------------------------------------
+
+@pytest.mark.parametrize("L", [128 * 6, 128 * 6 + 1, 128 * 5 + 77])
+def test_decode_equals_last_prefill_row(L):
+    """A decode step with a cache of L tokens is prefill row L-1. Catches a decode
+    query placed at position L instead of L-1 and a wrong partial last block."""
+    G, Hpg, D, d_idx, k = 2, 2, 16, 8, 3
+    x = _small(T=L, G=G, Hpg=Hpg, D=D, d_idx=d_idx, seed=L)
+    pre = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k=k, rows=[L - 1])
+    dec = orc.decode(x["q"][L - 1][None], x["k"][None], x["v"][None], x["q_idx"][L - 1][None],
+                     x["k_idx"][None], np.array([L]), top_k=k)
+    assert np.max(np.abs(pre["out"][0] - dec["out"][0])) < 1e-13
+    for g in range(G):
+        assert pre["sel"][0][g].tolist() == dec["sel"][0][g].tolist()
+    dd = orc.dense_decode(x["q"][L - 1][None], x["k"][None], x["v"][None], np.array([L]))
+    ref = _sdpa(x["q"], x["k"], x["v"], causal=True)[L - 1]
+    assert np.max(np.abs(dd[0] - ref)) < 1e-12
+
+
+def test_ragged_decode_uses_each_length():
+    """Two sequences of different lengths in one cache: each equals its own dense
+    reference at k = all blocks (catches reading past seq_len)."""
+    G, Hpg, D = 2, 2, 16
+    x = synth.decode_inputs(2, 600, G, Hpg, D, 8, dtype="f32", seed=3, seq_lens=[600, 301])
+    res = orc.decode(x["q"], x["k_cache"], x["v_cache"], x["q_idx"], x["k_idx"],
+                     x["seq_lens"], top_k=8)
+    for bi, L in enumerate([600, 301]):
+        q = x["q"][bi][None].expand(L, -1, -1)
+        ref = _sdpa(q, x["k_cache"][bi, :, :L], x["v_cache"][bi, :, :L])[0]
+        assert np.max(np.abs(res["out"][bi] - ref)) < 1e-12
+
+
+# -- Permutation invariance of the attention over a selection ------------------------
+
+def test_attend_is_order_free_and_softmax_sums():
+    """Exact softmax: output unchanged under a key permutation, and equal to the
+    closed form for two keys (p = 1 / (1 + exp(-(l1 - l2))))."""
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((3, 8))
+    kk = rng.standard_normal((50, 8))
+    vv = rng.standard_normal((50, 8))
+    perm = rng.permutation(50)
+    a = orc.attend(q, kk, vv, 0.3)
+    b = orc.attend(q, kk[perm], vv[perm], 0.3)
+    assert np.max(np.abs(a - b)) < 1e-13
+    q1 = np.array([[1.0, 0.0]])
+    k2 = np.array([[2.0, 0.0], [0.0, 0.0]])
+    v2 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o = orc.attend(q1, k2, v2, 0.5)
+    p = 1.0 / (1.0 + math.exp(-1.0))
+    assert abs(o[0, 0] - p) < 1e-15 and abs(o[0, 1] - (1 - p)) < 1e-15
