@@ -1,0 +1,290 @@
+// Index branch of MSA: token scores Q_idx . K_idx^T fused with 128-token block max
+// pooling (mlqm.cn blog on the MiniMax M3 sparse attention, section 2.1: one index
+// query per GQA group, one shared index-key head, block max pooling).
+//
+// Prefill kernel: the index queries of all groups form one [rows = tokens*G, d] matrix
+// and each workgroup owns 256 consecutive rows. It sweeps the key blocks
+// 0..b-1 (b = local block of its last row) in order; each block of index keys is
+// staged once in LDS (double-buffered) and shared by the 4 waves. The MFMA is
+// oriented as S^T = K_idx . Q_idx^T so that the 32 keys of a tile sit in the
+// accumulator registers of each lane (lane = query row): the block max is an
+// in-lane max plus one cross-half exchange, and only the block maxima are written.
+//
+// Decode kernel: streams k_idx[b] once at HBM rate. Each wave scores whole 128-key
+// blocks for up to 16 groups at a time on 16x16 MFMAs, K operands loaded straight
+// from global memory into registers (16 B per lane, all 32 loads of a block issued
+// before the first MFMA).
+#include "msa_device.h"
+#include "msa_launch.h"
+
+namespace msa {
+
+template <class E>
+struct Operand;
+template <>
+struct Operand<BF16> {
+  typedef u32x4 type;
+  static __device__ __forceinline__ type load(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+  }
+  static __device__ __forceinline__ type zero() { return u32x4{0u, 0u, 0u, 0u}; }
+};
+template <>
+struct Operand<F32> {
+  typedef float type;
+  static __device__ __forceinline__ type load(const float* p) { return *p; }
+  static __device__ __forceinline__ type zero() { return 0.f; }
+};
+
+// ------------------------------------------------------------------------------------
+// Prefill
+// ------------------------------------------------------------------------------------
+template <class E, int DI>
+struct PrefillCfg {
+  typedef typename E::elem elem;
+  static constexpr int kPad = E::is_bf16 ? 8 : 1;    // LDS row padding (elements)
+  static constexpr int kRow = DI + kPad;             // LDS row stride (elements)
+  static constexpr int kBuf = kBlock * kRow;         // one staged key block
+  static constexpr int kStep = 2 * E::kPerLane;      // dims per 32x32 MFMA k-step
+  static constexpr int kNStep = DI / kStep;
+  static constexpr int kChunkElems = 16 / sizeof(elem);
+  static constexpr int kChunks = kBlock * DI / kChunkElems;  // 16-byte chunks per block
+  static constexpr int kChunksPerThread = kChunks / 256;
+};
+
+template <class E, int DI>
+__global__ __launch_bounds__(256, 2) void index_scores_prefill_kernel(
+    const typename E::elem* __restrict__ q_idx, const typename E::elem* __restrict__ k_idx,
+    float* __restrict__ block_scores, int64_t q_begin, int64_t q_count, int G, int top_k,
+    int nblk) {
+  typedef PrefillCfg<E, DI> C;
+  typedef typename E::elem elem;
+  typedef typename Operand<E>::type op_t;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  elem* lds = reinterpret_cast<elem*>(smem_raw);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nrows = q_count * G;
+  // Heaviest (latest) rows first: causal work grows with the row's position.
+  const int64_t r0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * 256;
+  const int64_t r_last = min(r0 + 255, nrows - 1);
+  const int cmax = (int)((q_begin + r_last / G) / kBlock);
+  if (cmax < top_k) return;  // every row keeps all its visible blocks: nothing to score
+
+  // This lane's B operands (index query rows), two 32-row tiles per wave.
+  op_t qop[2][C::kNStep];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int64_t R = r0 + 64 * wave + 32 * rt + (lane & 31);
+    const bool ok = R < nrows;
+    const elem* qp = q_idx + (q_begin * G + (ok ? R : 0)) * DI + (lane >> 5) * E::kPerLane;
+#pragma unroll
+    for (int s = 0; s < C::kNStep; ++s)
+      qop[rt][s] = ok ? Operand<E>::load(qp + s * C::kStep) : Operand<E>::zero();
+  }
+  // The row this lane writes: lanes 0-31 tile 0, lanes 32-63 tile 1.
+  const int64_t Rw = r0 + 64 * wave + lane;
+  int bw = -1;
+  if (Rw < nrows) bw = (int)((q_begin + Rw / G) / kBlock);
+  const bool writes = bw >= top_k;
+  float* out_row = block_scores + (Rw < nrows ? Rw : 0) * (int64_t)nblk;
+
+  // Staging of one key block: thread-strided 16-byte chunks.
+  u32x4 stage[C::kChunksPerThread];
+  auto load_block = [&](int c) {
+    const elem* src = k_idx + (int64_t)c * kBlock * DI;
+#pragma unroll
+    for (int i = 0; i < C::kChunksPerThread; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      stage[i] = *reinterpret_cast<const u32x4*>(src + ch * C::kChunkElems);
+    }
+  };
+  auto store_block = [&](int buf) {
+    elem* dst = lds + buf * C::kBuf;
+#pragma unroll
+    for (int i = 0; i < C::kChunksPerThread; ++i) {
+      const int ch = threadIdx.x + 256 * i;
+      const int row = ch / (DI / C::kChunkElems);
+      const int col = (ch % (DI / C::kChunkElems)) * C::kChunkElems;
+      if constexpr (E::is_bf16) {
+        *reinterpret_cast<u32x4*>(dst + row * C::kRow + col) = stage[i];
+      } else {
+        float* d = reinterpret_cast<float*>(dst) + row * C::kRow + col;
+        d[0] = __uint_as_float(stage[i][0]);
+        d[1] = __uint_as_float(stage[i][1]);
+        d[2] = __uint_as_float(stage[i][2]);
+        d[3] = __uint_as_float(stage[i][3]);
+      }
+    }
+  };
+
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int c = 0; c < cmax; ++c) {
+    const bool has_next = c + 1 < cmax;
+    if (has_next) load_block(c + 1);
+    const elem* kb = lds + (c & 1) * C::kBuf + (lane & 31) * C::kRow + (lane >> 5) * E::kPerLane;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; kt += 2) {
+      f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
+#pragma unroll
+      for (int s = 0; s < C::kNStep; ++s) {
+        const op_t ka = Operand<E>::load(kb + (kt * 32) * C::kRow + s * C::kStep);
+        const op_t kc = Operand<E>::load(kb + (kt * 32 + 32) * C::kRow + s * C::kStep);
+        a00 = mfma32(ka, qop[0][s], a00);
+        a01 = mfma32(ka, qop[1][s], a01);
+        a10 = mfma32(kc, qop[0][s], a10);
+        a11 = mfma32(kc, qop[1][s], a11);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mx0 = fmaxf(mx0, fmaxf(a00[r], a10[r]));
+        mx1 = fmaxf(mx1, fmaxf(a01[r], a11[r]));
+      }
+    }
+    mx0 = fmaxf(mx0, __shfl_xor(mx0, 32, 64));
+    mx1 = fmaxf(mx1, __shfl_xor(mx1, 32, 64));
+    const float val = lane < 32 ? mx0 : mx1;
+    if (writes && c < bw) out_row[c] = val;
+    if (has_next) store_block((c + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Decode
+// ------------------------------------------------------------------------------------
+template <class E, int DI>
+__global__ __launch_bounds__(256) void index_scores_decode_kernel(
+    const typename E::elem* __restrict__ q_idx, const typename E::elem* __restrict__ k_idx,
+    float* __restrict__ block_scores, const int32_t* __restrict__ seq_lens, int64_t max_len,
+    int G, int top_k, int nblk, int blocks_per_wg) {
+  typedef typename E::elem elem;
+  typedef typename Operand<E>::type op_t;
+  constexpr int kStep = 4 * E::kPerLane;  // dims per 16x16 MFMA k-step
+  constexpr int kNStep = DI / kStep;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  int64_t L = seq_lens[b];
+  L = L < 1 ? 1 : (L > max_len ? max_len : L);
+  const int bl = (int)((L - 1) / kBlock);
+  if (bl < top_k) return;
+  const int c0 = blockIdx.x * blocks_per_wg;
+  if (c0 >= bl) return;
+  const int c1 = min(c0 + blocks_per_wg, bl);
+  const elem* kbase = k_idx + (int64_t)b * max_len * DI;
+
+  for (int g0 = 0; g0 < G; g0 += 16) {
+    const int gq = g0 + (lane & 15);
+    op_t qop[kNStep];
+    {
+      const bool ok = gq < G;
+      const elem* qp = q_idx + ((int64_t)b * G + (ok ? gq : 0)) * DI + (lane >> 4) * E::kPerLane;
+#pragma unroll
+      for (int s = 0; s < kNStep; ++s)
+        qop[s] = ok ? Operand<E>::load(qp + s * kStep) : Operand<E>::zero();
+    }
+    for (int c = c0 + wave; c < c1; c += 4) {
+      const elem* kp = kbase + ((int64_t)c * kBlock + (lane & 15)) * DI + (lane >> 4) * E::kPerLane;
+      // bf16: the whole block's operands (32 x 16 B per lane) are in flight before the
+      // first MFMA; fp32 (a correctness configuration) loads one 16-key tile at a time.
+      constexpr int kGroup = E::is_bf16 ? 8 : 1;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kg = 0; kg < 8; kg += kGroup) {
+        op_t ka[kGroup][kNStep];
+#pragma unroll
+        for (int kt = 0; kt < kGroup; ++kt)
+#pragma unroll
+          for (int s = 0; s < kNStep; ++s)
+            ka[kt][s] = Operand<E>::load(kp + (kg + kt) * 16 * DI + s * kStep);
+#pragma unroll
+        for (int kt = 0; kt < kGroup; ++kt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < kNStep; ++s) acc = mfma16(ka[kt][s], qop[s], acc);
+          mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (lane < 16 && gq < G) block_scores[((int64_t)b * G + gq) * nblk + c] = mx;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------------------
+template <class E, int DI>
+static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, float* bs,
+                                   int64_t q_begin, int64_t q_count, int G, int top_k, int nblk,
+                                   hipStream_t st) {
+  typedef PrefillCfg<E, DI> C;
+  const int64_t rows = q_count * G;
+  const int64_t grid = (rows + 255) / 256;
+  const size_t lds = 2 * C::kBuf * sizeof(typename E::elem);
+  hipLaunchKernelGGL((index_scores_prefill_kernel<E, DI>), dim3((unsigned)grid), dim3(256), lds,
+                     st, (const typename E::elem*)q_idx, (const typename E::elem*)k_idx, bs,
+                     q_begin, q_count, G, top_k, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_prefill(int bf16, int index_dim, const void* q_idx,
+                                       const void* k_idx, float* block_scores, int64_t q_begin,
+                                       int64_t q_count, int G, int top_k, int nblk,
+                                       hipStream_t stream) {
+  if (bf16) {
+    if (index_dim == 128)
+      return launch_prefill_t<BF16, 128>(q_idx, k_idx, block_scores, q_begin, q_count, G, top_k,
+                                         nblk, stream);
+    return launch_prefill_t<BF16, 64>(q_idx, k_idx, block_scores, q_begin, q_count, G, top_k,
+                                      nblk, stream);
+  }
+  if (index_dim == 128)
+    return launch_prefill_t<F32, 128>(q_idx, k_idx, block_scores, q_begin, q_count, G, top_k,
+                                      nblk, stream);
+  return launch_prefill_t<F32, 64>(q_idx, k_idx, block_scores, q_begin, q_count, G, top_k, nblk,
+                                   stream);
+}
+
+template <class E, int DI>
+static hipError_t launch_decode_t(const void* q_idx, const void* k_idx, float* bs,
+                                  const int32_t* seq_lens, int B, int64_t max_len, int G,
+                                  int top_k, int nblk, hipStream_t st) {
+  // Enough workgroups to cover the chip several times over at long contexts,
+  // each sweeping a contiguous run of blocks (multiple of the 4 waves).
+  const int64_t total = (int64_t)B * nblk;
+  int64_t per = (total + 2047) / 2048;
+  per = per < 4 ? 4 : (per > 64 ? 64 : per);
+  per = (per + 3) / 4 * 4;
+  const int gx = (int)((nblk + per - 1) / per);
+  hipLaunchKernelGGL((index_scores_decode_kernel<E, DI>), dim3(gx, B), dim3(256), 0, st,
+                     (const typename E::elem*)q_idx, (const typename E::elem*)k_idx, bs, seq_lens,
+                     max_len, G, top_k, nblk, (int)per);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_decode(int bf16, int index_dim, const void* q_idx,
+                                      const void* k_idx, float* block_scores,
+                                      const int32_t* seq_lens, int B, int64_t max_len, int G,
+                                      int top_k, int nblk, hipStream_t stream) {
+  if (bf16) {
+    if (index_dim == 128)
+      return launch_decode_t<BF16, 128>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G,
+                                        top_k, nblk, stream);
+    return launch_decode_t<BF16, 64>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
+                                     nblk, stream);
+  }
+  if (index_dim == 128)
+    return launch_decode_t<F32, 128>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
+                                     nblk, stream);
+  return launch_decode_t<F32, 64>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
+                                  nblk, stream);
+}
+
+}  // namespace msa

@@ -1,0 +1,254 @@
+// Host side of the MSA C ABI (include/msa.h): argument validation, workspace sizing
+// and launch configuration. Every check runs before any HIP call, so a rejected call
+// never touches the device. The library keeps no state and never allocates or syncs.
+#include "msa.h"
+
+#include <hip/hip_runtime.h>
+
+#include "msa_launch.h"
+
+using namespace msa;
+
+namespace {
+
+constexpr int64_t kMaxLen = int64_t(1) << 30;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* ptr) { return ptr != nullptr && (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+msa_status check_problem(const msa_problem* p) {
+  if (p == nullptr) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MSA_DTYPE_F32 && p->dtype != MSA_DTYPE_BF16) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->mode != MSA_MODE_PREFILL && p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->num_groups < 1 || p->heads_per_group < 1 || p->head_dim < 1 || p->index_dim < 1 ||
+      p->block_size < 1 || p->top_k < 1)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->num_groups > MSA_MAX_GROUPS || p->heads_per_group > MSA_MAX_HEADS_PER_GROUP)
+    return MSA_ERR_UNSUPPORTED;
+  if (p->head_dim != MSA_HEAD_DIM || p->block_size != MSA_BLOCK_SIZE) return MSA_ERR_UNSUPPORTED;
+  if (p->index_dim != 64 && p->index_dim != 128) return MSA_ERR_UNSUPPORTED;
+  if (p->top_k > MSA_MAX_TOPK) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->mode == MSA_MODE_PREFILL) {
+    if (p->seq_len < 1 || p->seq_len > kMaxLen) return MSA_ERR_INVALID_ARGUMENT;
+    if (p->q_begin < 0 || p->q_count < 0 || p->q_begin + p->q_count > p->seq_len)
+      return MSA_ERR_INVALID_ARGUMENT;
+    if (p->algo < MSA_ALGO_AUTO || p->algo > MSA_ALGO_KV_CENTRIC) return MSA_ERR_INVALID_ARGUMENT;
+  } else {
+    if (p->batch < 1 || p->batch > 65535) return MSA_ERR_INVALID_ARGUMENT;
+    if (p->max_len < 1 || p->max_len > kMaxLen) return MSA_ERR_INVALID_ARGUMENT;
+    if (p->seq_lens == nullptr || (reinterpret_cast<uintptr_t>(p->seq_lens) & 3u) != 0)
+      return MSA_ERR_INVALID_ARGUMENT;
+  }
+  return MSA_OK;
+}
+
+int64_t nblk_of(const msa_problem* p) {
+  return ceil_div(p->mode == MSA_MODE_PREFILL ? p->seq_len : p->max_len, MSA_BLOCK_SIZE);
+}
+
+// Decode split-K plan: sparse uses one kept block per split; dense spreads the cache
+// blocks so that the launch has a few thousand waves.
+void decode_split(const msa_problem* p, bool dense, int* nsplit, int* bps) {
+  if (!dense) {
+    *nsplit = p->top_k;
+    *bps = 1;
+    return;
+  }
+  const int64_t nblk = nblk_of(p);
+  int64_t per = ceil_div((int64_t)p->batch * p->num_groups * nblk, 4096);
+  if (per < 1) per = 1;
+  *bps = (int)per;
+  *nsplit = (int)ceil_div(nblk, per);
+}
+
+size_t decode_ws_bytes(const msa_problem* p, bool dense) {
+  int nsplit, bps;
+  decode_split(p, dense, &nsplit, &bps);
+  const size_t units = (size_t)p->batch * p->num_groups * nsplit * p->heads_per_group;
+  return align_up(units * MSA_HEAD_DIM * sizeof(float)) + align_up(units * 2 * sizeof(float));
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q, const void* k,
+                                const void* v, const int32_t* block_idx, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t st) {
+  const size_t need = decode_ws_bytes(p, dense);
+  if (workspace_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
+  int nsplit, bps;
+  decode_split(p, dense, &nsplit, &bps);
+  const size_t units = (size_t)p->batch * p->num_groups * nsplit * p->heads_per_group;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            align_up(units * MSA_HEAD_DIM * sizeof(float)));
+  GatherParams gp = {};
+  gp.mode = dense ? kDecodeDense : kDecodeSparse;
+  gp.bf16 = p->dtype == MSA_DTYPE_BF16;
+  gp.q = q;
+  gp.k = k;
+  gp.v = v;
+  gp.block_idx = block_idx;
+  gp.part_o = part_o;
+  gp.part_ml = part_ml;
+  gp.G = p->num_groups;
+  gp.Hpg = p->heads_per_group;
+  gp.top_k = p->top_k;
+  gp.seq_lens = p->seq_lens;
+  gp.B = p->batch;
+  gp.max_len = p->max_len;
+  gp.nsplit = nsplit;
+  gp.blocks_per_split = bps;
+  hipError_t e = launch_gather_attn(gp, st);
+  if (e != hipSuccess) return MSA_ERR_HIP;
+  return hip_status(launch_decode_combine(gp.bf16, part_o, part_ml, out, p->batch, p->num_groups,
+                                          p->heads_per_group, nsplit, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT: bad pointer, range or enum";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: dimension or option not built";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL: see msa_workspace_size";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch failed";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes) {
+  if (bytes == nullptr) return MSA_ERR_INVALID_ARGUMENT;
+  *bytes = 0;
+  const msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  switch (entry) {
+    case MSA_ENTRY_INDEX_SCORES:
+    case MSA_ENTRY_BLOCK_TOPK:
+      return MSA_OK;
+    case MSA_ENTRY_SPARSE_ATTN_PREFILL:
+      if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
+      return MSA_OK;
+    case MSA_ENTRY_SPARSE_ATTN_DECODE:
+      if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+      *bytes = decode_ws_bytes(p, false);
+      return MSA_OK;
+    case MSA_ENTRY_DENSE_GQA_ATTN:
+      if (p->mode == MSA_MODE_DECODE) *bytes = decode_ws_bytes(p, true);
+      return MSA_OK;
+    default:
+      return MSA_ERR_INVALID_ARGUMENT;
+  }
+}
+
+msa_status msa_index_scores(const msa_problem* p, const void* q_idx, const void* k_idx,
+                            float* block_scores, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_scores))
+    return MSA_ERR_INVALID_ARGUMENT;
+  const int bf16 = p->dtype == MSA_DTYPE_BF16;
+  const int nblk = (int)nblk_of(p);
+  if (p->mode == MSA_MODE_PREFILL) {
+    if (p->q_count == 0) return MSA_OK;
+    return hip_status(launch_index_scores_prefill(bf16, p->index_dim, q_idx, k_idx, block_scores,
+                                                  p->q_begin, p->q_count, p->num_groups,
+                                                  p->top_k, nblk, as_stream(stream)));
+  }
+  return hip_status(launch_index_scores_decode(bf16, p->index_dim, q_idx, k_idx, block_scores,
+                                               p->seq_lens, p->batch, p->max_len,
+                                               p->num_groups, p->top_k, nblk, as_stream(stream)));
+}
+
+msa_status msa_block_topk(const msa_problem* p, const float* block_scores, int32_t* block_idx,
+                          void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (!aligned16(block_scores) || !aligned16(block_idx)) return MSA_ERR_INVALID_ARGUMENT;
+  const bool decode = p->mode == MSA_MODE_DECODE;
+  const int64_t rows = (decode ? (int64_t)p->batch : p->q_count) * p->num_groups;
+  if (rows == 0) return MSA_OK;
+  return hip_status(launch_block_topk(block_scores, block_idx, rows, p->num_groups,
+                                      (int)nblk_of(p), p->top_k, decode ? 1 : 0, p->q_begin,
+                                      p->seq_lens, p->max_len, as_stream(stream)));
+}
+
+msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
+                                   const void* v, const int32_t* block_idx, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  (void)workspace;
+  (void)workspace_bytes;
+  if (p->q_count == 0) return MSA_OK;
+  GatherParams gp = {};
+  gp.mode = kPrefillSparse;
+  gp.bf16 = p->dtype == MSA_DTYPE_BF16;
+  gp.q = q;
+  gp.k = k;
+  gp.v = v;
+  gp.block_idx = block_idx;
+  gp.out = out;
+  gp.G = p->num_groups;
+  gp.Hpg = p->heads_per_group;
+  gp.top_k = p->top_k;
+  gp.q_begin = p->q_begin;
+  gp.q_count = p->q_count;
+  gp.seq_len = p->seq_len;
+  return hip_status(launch_gather_attn(gp, as_stream(stream)));
+}
+
+msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_idx, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_idx) ||
+      !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
+                              workspace_bytes, as_stream(stream));
+}
+
+msa_status msa_dense_gqa_attn(const msa_problem* p, const void* q, const void* k, const void* v,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->mode == MSA_MODE_DECODE)
+    return run_decode_attention(p, true, q, k, v, nullptr, out, workspace, workspace_bytes,
+                                as_stream(stream));
+  if (p->q_count == 0) return MSA_OK;
+  GatherParams gp = {};
+  gp.mode = kPrefillDense;
+  gp.bf16 = p->dtype == MSA_DTYPE_BF16;
+  gp.q = q;
+  gp.k = k;
+  gp.v = v;
+  gp.out = out;
+  gp.G = p->num_groups;
+  gp.Hpg = p->heads_per_group;
+  gp.top_k = p->top_k;
+  gp.q_begin = p->q_begin;
+  gp.q_count = p->q_count;
+  gp.seq_len = p->seq_len;
+  return hip_status(launch_gather_attn(gp, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device helpers shared by the MSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 128;
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bf16 storage is raw uint16_t --------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Round to nearest even; inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- element traits -----------------------------------------------------------------
+// Operand of one MFMA k-step per lane: 8 bf16 (16 B) or 1 fp32.
+struct BF16 {
+  typedef uint16_t elem;
+  static constexpr int kPerLane = 8;       // elements per lane per MFMA k-step
+  static constexpr bool is_bf16 = true;
+};
+struct F32 {
+  typedef float elem;
+  static constexpr int kPerLane = 1;
+  static constexpr bool is_bf16 = false;
+};
+
+__device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float x) {
+  *p = (uint16_t)f32_to_bf16_bits(x);
+}
+__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+
+// ---- MFMA wrappers --------------------------------------------------------------------
+// 32x32 output tile. Lane l holds column l % 32 and rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// 16x16 output tile. Lane l holds column l % 16 and rows 4*(l/16) + r, r < 4.
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- ordered keys for top-k -------------------------------------------------------------
+// Monotone map of finite floats to uint32 (a < b  <=>  key(a) < key(b)); -0.0 == +0.0.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_max_xor(float x, int from_mask) {
+  // Max over lanes that differ only in bits >= from_mask (from_mask a power of two).
+  for (int m = from_mask; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor(float x, int from_mask) {
+  for (int m = from_mask; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace msa

@@ -1,0 +1,53 @@
+// Host-side launchers of the MSA kernels (internal; the public ABI is include/msa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+// All launchers enqueue on `stream` and return hipGetLastError() of their launches.
+hipError_t launch_index_scores_prefill(int bf16, int index_dim, const void* q_idx,
+                                       const void* k_idx, float* block_scores, int64_t q_begin,
+                                       int64_t q_count, int G, int top_k, int nblk,
+                                       hipStream_t stream);
+
+hipError_t launch_index_scores_decode(int bf16, int index_dim, const void* q_idx,
+                                      const void* k_idx, float* block_scores,
+                                      const int32_t* seq_lens, int B, int64_t max_len, int G,
+                                      int top_k, int nblk, hipStream_t stream);
+
+hipError_t launch_block_topk(const float* block_scores, int32_t* block_idx, int64_t rows, int G,
+                             int nblk, int top_k, int decode, int64_t q_begin,
+                             const int32_t* seq_lens, int64_t max_len, hipStream_t stream);
+
+// Gather attention: one wave per (query, group[, split]); see attn_gather.hip.
+enum GatherMode { kPrefillSparse = 0, kPrefillDense = 1, kDecodeSparse = 2, kDecodeDense = 3 };
+
+struct GatherParams {
+  int mode;
+  int bf16;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_idx;  // sparse modes
+  void* out;                 // prefill: final output
+  float* part_o;             // decode: [units][Hpg][128] unnormalised partial outputs
+  float* part_ml;            // decode: [units][Hpg][2] (running max in log2 units, sum)
+  int G, Hpg, top_k;
+  int64_t q_begin, q_count, seq_len;  // prefill
+  const int32_t* seq_lens;            // decode
+  int B;
+  int64_t max_len;
+  int nsplit;            // decode: splits per (sequence, group)
+  int blocks_per_split;  // decode
+};
+
+hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);
+
+// Fixed-order log-sum-exp merge of decode partials into out [B, Hq, 128].
+hipError_t launch_decode_combine(int bf16, const float* part_o, const float* part_ml, void* out,
+                                 int B, int G, int Hpg, int nsplit, hipStream_t stream);
+
+}  // namespace msa

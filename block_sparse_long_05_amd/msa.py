@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libmsa.so (include/msa.h).
+
+Argument marshalling only: torch tensors become raw device pointers and the current
+HIP stream; every step of the hot path runs in the library's kernels. There is no
+fallback: if libmsa.so is missing the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK = 0
+MSA_ERR_INVALID_ARGUMENT = 1
+MSA_ERR_UNSUPPORTED = 2
+MSA_ERR_WORKSPACE_TOO_SMALL = 3
+MSA_ERR_HIP = 4
+
+DTYPE = {"f32": 0, "bf16": 1}
+MODE = {"prefill": 0, "decode": 1}
+ENTRY = {"index_scores": 0, "block_topk": 1, "sparse_attn_prefill": 2,
+         "sparse_attn_decode": 3, "dense_gqa_attn": 4}
+ALGO = {"auto": 0, "query_centric": 1, "kv_centric": 2}
+
+BLOCK = 128
+
+# Every symbol include/msa.h declares.
+EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_sparse_attn_prefill",
+            "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
+            "msa_status_string", "msa_abi_version"]
+
+
+class CProblem(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("mode", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+        ("heads_per_group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("seq_len", ctypes.c_int64), ("q_begin", ctypes.c_int64), ("q_count", ctypes.c_int64),
+        ("batch", ctypes.c_int32), ("algo", ctypes.c_int32), ("max_len", ctypes.c_int64),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmsa.so (built by build.py / __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first "
+                           "(python -m block_sparse_long_05_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pp = ctypes.POINTER(CProblem)
+    lib.msa_index_scores.argtypes = [pp, vp, vp, vp, vp]
+    lib.msa_block_topk.argtypes = [pp, vp, vp, vp]
+    lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(sz)]
+    lib.msa_status_string.argtypes = [ctypes.c_int]
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_abi_version.argtypes = []
+    for name in ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_prefill",
+                 "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
+                 "msa_abi_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().msa_status_string(int(status)).decode()
+
+
+@dataclass
+class Problem:
+    """Python mirror of msa_problem (see include/msa.h for every field)."""
+    dtype: str
+    mode: str
+    num_groups: int
+    heads_per_group: int
+    index_dim: int
+    top_k: int
+    head_dim: int = 128
+    block_size: int = BLOCK
+    seq_len: int = 0
+    q_begin: int = 0
+    q_count: int = 0
+    batch: int = 0
+    algo: str = "auto"
+    max_len: int = 0
+    seq_lens: Optional[torch.Tensor] = None  # device int32 [B]
+    _c: Optional[CProblem] = None
+
+    def c(self) -> CProblem:
+        sl = self.seq_lens
+        self._c = CProblem(DTYPE[self.dtype], MODE[self.mode], self.num_groups,
+                           self.heads_per_group, self.head_dim, self.index_dim, self.block_size,
+                           self.top_k, self.seq_len, self.q_begin, self.q_count, self.batch,
+                           ALGO[self.algo], self.max_len, 0 if sl is None else sl.data_ptr())
+        return self._c
+
+    @property
+    def nblk(self) -> int:
+        n = self.seq_len if self.mode == "prefill" else self.max_len
+        return (n + BLOCK - 1) // BLOCK
+
+    @property
+    def rows(self) -> int:
+        return self.q_count if self.mode == "prefill" else self.batch
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        if x.device.type != "cuda":
+            raise ValueError("MSA tensors must live in device memory")
+        if not x.is_contiguous():
+            raise ValueError("MSA tensors must be contiguous")
+        return x.data_ptr()
+    raise TypeError(type(x))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MSA_OK:
+        raise MsaError(status, where)
+
+
+def msa_workspace_size(p: Problem, entry: str) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_workspace_size(ctypes.byref(p.c()), ENTRY[entry], ctypes.byref(n)),
+           "msa_workspace_size")
+    return int(n.value)
+
+
+def msa_index_scores(p: Problem, q_idx, k_idx, block_scores, stream=None):
+    _check(load_library().msa_index_scores(ctypes.byref(p.c()), _ptr(q_idx), _ptr(k_idx),
+                                           _ptr(block_scores), _stream(stream)),
+           "msa_index_scores")
+
+
+def msa_block_topk(p: Problem, block_scores, block_idx, stream=None):
+    _check(load_library().msa_block_topk(ctypes.byref(p.c()), _ptr(block_scores), _ptr(block_idx),
+                                         _stream(stream)), "msa_block_topk")
+
+
+def msa_sparse_attn_prefill(p: Problem, q, k, v, block_idx, out, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_sparse_attn_prefill(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_prefill")
+
+
+def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, block_idx, out, workspace=None,
+                           stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_sparse_attn_decode(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_idx), _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode")
+
+
+def msa_dense_gqa_attn(p: Problem, q, k, v, out, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_dense_gqa_attn(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace), ws_bytes,
+        _stream(stream)), "msa_dense_gqa_attn")
+
+
+# ---- buffer helpers (allocation stays with the caller, i.e. torch) -----------------------
+
+def alloc_workspace(p: Problem, entry: str, device="cuda") -> Optional[torch.Tensor]:
+    n = msa_workspace_size(p, entry)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_block_scores(p: Problem, device="cuda") -> torch.Tensor:
+    return torch.empty((p.rows, p.num_groups, p.nblk), dtype=torch.float32, device=device)
+
+
+def alloc_block_idx(p: Problem, device="cuda") -> torch.Tensor:
+    return torch.empty((p.rows, p.num_groups, p.top_k), dtype=torch.int32, device=device)
+
+
+# ---- the whole hot path, as a chain of the C calls ------------------------------------------
+
+def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None,
+            algo: str = "auto", out=None, block_scores=None, block_idx=None, workspace=None,
+            stream=None):
+    """MSA prefill of query rows [q_begin, q_begin + q_count): index scores -> top-k ->
+    sparse attention. x holds q, k, v, q_idx, k_idx on the device. Returns
+    (out, block_idx, block_scores)."""
+    q = x["q"]
+    T, Hq, D = q.shape
+    G = x["k"].shape[0]
+    if q_count is None:
+        q_count = T - q_begin
+    p = Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="prefill",
+                num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
+                top_k=top_k, head_dim=D, seq_len=T, q_begin=q_begin, q_count=q_count, algo=algo)
+    if out is None:
+        out = torch.empty_like(q)
+    if block_scores is None:
+        block_scores = alloc_block_scores(p, q.device)
+    if block_idx is None:
+        block_idx = alloc_block_idx(p, q.device)
+    if workspace is None:
+        workspace = alloc_workspace(p, "sparse_attn_prefill", q.device)
+    msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
+    msa_block_topk(p, block_scores, block_idx, stream)
+    msa_sparse_attn_prefill(p, q, x["k"], x["v"], block_idx, out, workspace, stream)
+    return out, block_idx, block_scores
+
+
+def decode_problem(x: dict, top_k: int) -> Problem:
+    q = x["q"]
+    B, Hq, D = q.shape
+    G = x["k_cache"].shape[1]
+    return Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="decode",
+                   num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
+                   top_k=top_k, head_dim=D, batch=B, max_len=x["k_cache"].shape[2],
+                   seq_lens=x["seq_lens"])
+
+
+def decode(x: dict, top_k: int, out=None, block_scores=None, block_idx=None, workspace=None,
+           stream=None):
+    """One MSA decode step: index scan -> top-k -> split-K sparse attention + combine.
+    Returns (out, block_idx, block_scores)."""
+    p = decode_problem(x, top_k)
+    if out is None:
+        out = torch.empty_like(x["q"])
+    if block_scores is None:
+        block_scores = alloc_block_scores(p, x["q"].device)
+    if block_idx is None:
+        block_idx = alloc_block_idx(p, x["q"].device)
+    if workspace is None:
+        workspace = alloc_workspace(p, "sparse_attn_decode", x["q"].device)
+    msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
+    msa_block_topk(p, block_scores, block_idx, stream)
+    msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], block_idx, out, workspace,
+                           stream)
+    return out, block_idx, block_scores

@@ -70,9 +70,10 @@ def _randn(shape, dtype, device, gen):
 
 
 def _distinct_blocks(n_pick: int, n_blocks: int, gen: torch.Generator, device) -> torch.Tensor:
-    n_pick = min(n_pick, n_blocks)
-    perm = torch.randperm(n_blocks, generator=gen, device=device)
-    return perm[:n_pick].to("cpu")
+    """n_pick distinct block ids from [0, n_blocks), padded with -1 when there are fewer."""
+    perm = torch.randperm(n_blocks, generator=gen, device=device)[:n_pick].to("cpu")
+    pad = torch.full((n_pick - perm.numel(),), -1, dtype=perm.dtype)
+    return torch.cat([perm, pad])
 
 
 def prefill_inputs(T: int, G: int, Hpg: int, D: int = 128, d_idx: int = 128,
@@ -102,7 +103,8 @@ def prefill_inputs(T: int, G: int, Hpg: int, D: int = 128, d_idx: int = 128,
             blocks = _distinct_blocks(planted_per_group, n_full, gen_p, dev)
             rows.append(blocks)
             for c in blocks.tolist():
-                k_idx32[c * BLOCK:(c + 1) * BLOCK] += plant_scale * u[g]
+                if c >= 0:
+                    k_idx32[c * BLOCK:(c + 1) * BLOCK] += plant_scale * u[g]
         planted = torch.stack(rows)
         k_idx = k_idx32.to(dt)
         del k_idx32
@@ -151,7 +153,8 @@ def decode_inputs(B: int, max_len: int, G: int, Hpg: int, D: int = 128, d_idx: i
                 blocks = _distinct_blocks(planted_per_group, n_blk, gen_p, dev)
                 per_g.append(blocks)
                 for c in blocks.tolist():
-                    kb[c * BLOCK:min((c + 1) * BLOCK, max_len)] += plant_scale * q_idx32[b, g]
+                    if c >= 0:
+                        kb[c * BLOCK:min((c + 1) * BLOCK, max_len)] += plant_scale * q_idx32[b, g]
             per_b.append(torch.stack(per_g))
             k_idx[b].copy_(kb)
             del kb

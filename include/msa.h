@@ -1,0 +1,170 @@
+/*
+ * msa.h - C ABI of the MiniMax Sparse Attention (MSA) hot path on AMD gfx950 (MI355X).
+ *
+ * The method (researchpapers.dev summary "MiniMax Sparse Attention", section
+ * "Mechanism"; mlqm.cn blog on the MiniMax M3 sparse attention, sections 2.1-2.2):
+ *   Index branch - one index query per GQA group is dotted with a single shared
+ *     index-key head; token scores are max-pooled per 128-token block; per (query,
+ *     group) the top-k blocks are kept, the query's own (local) block always
+ *     included and future blocks never.
+ *   Main branch - every query head of the group runs exact softmax attention over
+ *     the keys of the kept blocks only (16 blocks x 128 tokens in the pages'
+ *     configuration), both for causal prefill and for single-token decode.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
+ *     row-major and 16-byte aligned. The library never allocates, frees, copies to
+ *     the host or synchronises; work is enqueued in order on `stream` (a
+ *     hipStream_t; NULL = the default stream). Calls are stateless and re-entrant.
+ *   - All argument checks run on the host before any launch, so every error return
+ *     below happens without touching the device. A failed launch returns
+ *     MSA_ERR_HIP; faults inside kernels surface at the caller's next sync.
+ *   - Float tensors other than block scores have the element type `dtype`
+ *     (fp32 or bf16); arithmetic accumulates in fp32; outputs round to nearest even.
+ *   - Shapes (G = num_groups, Hpg = heads_per_group, Hq = G*Hpg, D = head_dim,
+ *     d = index_dim, nblk = ceil(len / 128), head h belongs to group h / Hpg):
+ *       prefill  q [T, Hq, D]   k, v [G, T, D]   q_idx [T, G, d]   k_idx [T, d]
+ *                out [T, Hq, D]
+ *       decode   q [B, Hq, D]   k_cache, v_cache [B, G, max_len, D]
+ *                q_idx [B, G, d]   k_idx [B, max_len, d]   seq_lens [B] (int32)
+ *                out [B, Hq, D]
+ *     Full tensors are always passed whole; prefill calls work on query rows
+ *     [q_begin, q_begin + q_count) and the per-call intermediates (block scores,
+ *     block ids) hold only those rows ("chunk-relative").
+ *   - Inputs must be finite. NaN/Inf inputs give unspecified results (no fault).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+#define MSA_BLOCK_SIZE 128
+#define MSA_HEAD_DIM 128
+#define MSA_MAX_TOPK 64
+#define MSA_MAX_GROUPS 64
+#define MSA_MAX_HEADS_PER_GROUP 16
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad range, bad enum */
+  MSA_ERR_UNSUPPORTED = 2,         /* valid but not built: head_dim, index_dim, block size, ... */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < msa_workspace_size(...) */
+  MSA_ERR_HIP = 4                  /* a kernel launch failed */
+} msa_status;
+
+typedef enum { MSA_DTYPE_F32 = 0, MSA_DTYPE_BF16 = 1 } msa_dtype;
+typedef enum { MSA_MODE_PREFILL = 0, MSA_MODE_DECODE = 1 } msa_mode;
+
+/* Which entry point a workspace size is asked for. */
+typedef enum {
+  MSA_ENTRY_INDEX_SCORES = 0,
+  MSA_ENTRY_BLOCK_TOPK = 1,
+  MSA_ENTRY_SPARSE_ATTN_PREFILL = 2,
+  MSA_ENTRY_SPARSE_ATTN_DECODE = 3,
+  MSA_ENTRY_DENSE_GQA_ATTN = 4
+} msa_entry;
+
+/* Prefill main-branch algorithm. Both give the same result up to fp32 rounding. */
+typedef enum {
+  MSA_ALGO_AUTO = 0,           /* library choice (KV-centric when the workspace allows) */
+  MSA_ALGO_QUERY_CENTRIC = 1,  /* one wave per (token, group); no workspace */
+  MSA_ALGO_KV_CENTRIC = 2      /* reverse index: each kept block staged once for all its queries */
+} msa_algo;
+
+typedef struct msa_problem {
+  int32_t dtype;           /* msa_dtype of q, k, v, q_idx, k_idx, caches and out */
+  int32_t mode;            /* msa_mode */
+  int32_t num_groups;      /* G: GQA groups = KV heads = index queries per token, 1..64 */
+  int32_t heads_per_group; /* Hpg: query heads per group, 1..16 */
+  int32_t head_dim;        /* D: 128 */
+  int32_t index_dim;       /* d: 64 or 128 */
+  int32_t block_size;      /* 128 (selection and pooling granularity) */
+  int32_t top_k;           /* blocks kept per (query, group), local block included, 1..64 */
+  int64_t seq_len;         /* prefill: T, tokens in the sequence, 1..2^30 */
+  int64_t q_begin;         /* prefill: first query row of this call */
+  int64_t q_count;         /* prefill: query rows of this call (0 = nothing to do) */
+  int32_t batch;           /* decode: B, 1..65535 */
+  int32_t algo;            /* msa_algo (prefill sparse attention only) */
+  int64_t max_len;         /* decode: cache capacity in tokens, 1..2^30 */
+  const int32_t* seq_lens; /* decode: device int32[B]; each must be in [1, max_len]
+                              (values outside are clamped into that range) */
+} msa_problem;
+
+/*
+ * Index branch, step 1+2: token scores Q_idx . K_idx^T fused with 128-token block max
+ * pooling (mlqm.cn blog, section 2.1: single shared index key, block max pooling).
+ *   prefill: for chunk row i (token t = q_begin + i, local block b = t / 128) and
+ *     group g, writes block_scores[i, g, c] = max_{j in block c} q_idx[t, g] . k_idx[j]
+ *     for c < b, only when b >= top_k (otherwise every visible block is kept and no
+ *     score is needed). block_scores is fp32 [q_count, G, nblk], nblk = ceil(T/128).
+ *   decode: the same for the query at position L_b - 1 of sequence b, over
+ *     k_idx[b, :, :]; block_scores is fp32 [B, G, ceil(max_len/128)].
+ *   Entries not named above are left untouched. The token scores never reach memory.
+ */
+msa_status msa_index_scores(const msa_problem* p, const void* q_idx, const void* k_idx,
+                            float* block_scores, void* stream);
+
+/*
+ * Index branch, step 3: block selection (researchpapers.dev summary, "Mechanism":
+ * top-k blocks per query and group with the local block always kept).
+ * For each row: if b + 1 <= top_k, blocks 0..b; otherwise b plus the top_k - 1 best
+ * of blocks 0..b-1, ranked by score (higher first) then block index (lower first),
+ * with -0.0 equal to +0.0. block_idx is int32 [rows, G, top_k] (rows = q_count for
+ * prefill, B for decode), ascending, padded with -1. Reads only the block_scores
+ * entries that msa_index_scores writes.
+ */
+msa_status msa_block_topk(const msa_problem* p, const float* block_scores, int32_t* block_idx,
+                          void* stream);
+
+/*
+ * Main branch, prefill (mlqm.cn blog, section 2.2: gather the kept K/V blocks, then
+ * attention; every head of a group shares the group's selection): for chunk row i
+ * (token t = q_begin + i) and head h of group g,
+ *   out[t, h] = sum_j softmax_j(q[t, h] . k[g, j] / sqrt(D)) v[g, j]
+ * over the tokens j <= t of the blocks listed in block_idx[i, g, :]. Ids < 0 are
+ * padding; ids above the query's local block are ignored. Writes out rows
+ * [q_begin, q_begin + q_count). workspace may be NULL when
+ * msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_PREFILL) is 0 for the chosen algo.
+ */
+msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
+                                   const void* v, const int32_t* block_idx, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Main branch, decode: the same attention for the single query of each sequence
+ * (position L_b - 1) over the kept blocks of its cache, split over the kept blocks
+ * and merged with a log-sum-exp combine in a fixed order.
+ */
+msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_idx, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense GQA attention with the same heads (the baseline the researchpapers.dev summary
+ * compares MSA against, "Key results"). Prefill: causal attention of query rows
+ * [q_begin, q_begin + q_count) over keys j <= t. Decode: each sequence's query over
+ * its whole cache of L_b tokens. Used for speedup context only.
+ */
+msa_status msa_dense_gqa_attn(const msa_problem* p, const void* q, const void* k, const void* v,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that `entry` needs for problem p (0 if none). */
+msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status s);
+
+/* MSA_ABI_VERSION of the built library. */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

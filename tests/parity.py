@@ -1,0 +1,87 @@
+"""Comparison helpers for the GPU parity tests: HIP results vs the CPU oracle.
+
+Tolerances (outputs, max abs): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs with fp32
+accumulation. Selected block sets must match bit for bit except on rows the oracle
+declares near ties (relative gap < 1e-5 between the last selected and the first
+unselected block score, computed in fp64); such rows are counted, and their outputs
+are checked against the oracle's attention over the GPU's own selection.
+"""
+
+import numpy as np
+import torch
+
+from oracle import msa_oracle as orc
+
+OUT_TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# Block scores: fp32 accumulation of d_idx products against the fp64 oracle.
+SCORE_RTOL = 2e-5
+
+
+def np32(x):
+    return x.detach().float().cpu().numpy()
+
+
+def check_block_scores(bs_gpu, oracle_scores, row_map, label=""):
+    """oracle_scores {(i, g): fp64 scores of blocks 0..b-1}; row_map i -> gpu row."""
+    worst = 0.0
+    for (i, g), ref in oracle_scores.items():
+        got = bs_gpu[row_map(i), g, : len(ref)].astype(np.float64)
+        scale = np.maximum(1.0, np.abs(ref))
+        err = float(np.max(np.abs(got - ref) / scale)) if len(ref) else 0.0
+        worst = max(worst, err)
+    assert worst <= SCORE_RTOL, f"{label} block score rel err {worst}"
+    return worst
+
+
+def check_selection(idx_gpu, oracle_sel, near_tie, top_k, label=""):
+    """Returns the set of (i, g) rows whose selection differs (all near ties)."""
+    ref = orc.selection_array(oracle_sel, top_k)
+    diff = np.any(idx_gpu != ref, axis=2)
+    bad = diff & ~near_tie
+    assert not bad.any(), (
+        f"{label}: {int(bad.sum())} rows differ without a near tie, first "
+        f"{np.argwhere(bad)[:5].tolist()}")
+    return {tuple(x) for x in np.argwhere(diff).tolist()}
+
+
+def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, label=""):
+    """Compare a prefill run for oracle rows `rows` (absolute token ids)."""
+    dtype = x["q"].dtype
+    tol = OUT_TOL[dtype]
+    G = x["k"].shape[0]
+    Hpg = x["q"].shape[1] // G
+    rows = np.asarray(rows)
+    idx_rows = idx_gpu[rows - q_begin]
+    differ = check_selection(idx_rows, res["sel"], res["near_tie"], top_k, label)
+    if bs_gpu is not None:
+        check_block_scores(bs_gpu, res["block_scores"], lambda i: rows[i] - q_begin, label)
+    got = out_gpu[rows].astype(np.float64)
+    ref = res["out"].copy()
+    for (i, g) in differ:
+        t = int(rows[i])
+        hs = slice(g * Hpg, (g + 1) * Hpg)
+        ref[i, hs] = orc.attend_on_selection(x["q"][t, hs], x["k"][g], x["v"][g],
+                                             idx_rows[i, g], t)
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tol, f"{label}: max abs err {err} > {tol}"
+    return dict(err=err, near_ties=int(res["near_tie"].sum()), differ=len(differ))
+
+
+def check_decode(x, out_gpu, idx_gpu, bs_gpu, res, top_k, label=""):
+    dtype = x["q"].dtype
+    tol = OUT_TOL[dtype]
+    G = x["k_cache"].shape[1]
+    Hpg = x["q"].shape[1] // G
+    differ = check_selection(idx_gpu, res["sel"], res["near_tie"], top_k, label)
+    if bs_gpu is not None:
+        check_block_scores(bs_gpu, res["block_scores"], lambda i: i, label)
+    got = out_gpu.astype(np.float64)
+    ref = res["out"].copy()
+    lens = x["seq_lens"].cpu().numpy()
+    for (b, g) in differ:
+        hs = slice(g * Hpg, (g + 1) * Hpg)
+        ref[b, hs] = orc.attend_on_selection(x["q"][b, hs], x["k_cache"][b, g],
+                                             x["v_cache"][b, g], idx_gpu[b, g], int(lens[b]) - 1)
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tol, f"{label}: max abs err {err} > {tol}"
+    return dict(err=err, near_ties=int(res["near_tie"].sum()), differ=len(differ))

@@ -1,0 +1,143 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/msa.h declares, and rejects bad arguments on the host before any launch.
+No call here reaches a kernel, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_05_amd import msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(msa.LIB_PATH),
+                                reason="libmsa.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(msa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(msa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = msa.load_library()
+    assert lib.msa_abi_version() == 1
+    for s in range(5):
+        assert msa.status_string(s).startswith("MSA_")
+
+
+def _prefill(**kw):
+    base = dict(dtype="bf16", mode="prefill", num_groups=8, heads_per_group=8, index_dim=128,
+                top_k=16, seq_len=4096, q_begin=0, q_count=4096)
+    base.update(kw)
+    return msa.Problem(**base)
+
+
+def _call_index(p):
+    return msa.load_library().msa_index_scores(ctypes.byref(p.c()), FAKE, FAKE, FAKE, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(index_dim=96), msa.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), msa.MSA_ERR_UNSUPPORTED),
+    (dict(heads_per_group=17), msa.MSA_ERR_UNSUPPORTED),
+    (dict(num_groups=65), msa.MSA_ERR_UNSUPPORTED),
+    (dict(top_k=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(top_k=65), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(num_groups=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(q_begin=4000, q_count=200), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(q_begin=-1), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=0, q_count=0), msa.MSA_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=(1 << 30) + 1, q_count=1), msa.MSA_ERR_INVALID_ARGUMENT),
+])
+def test_prefill_validation(kw, code):
+    assert _call_index(_prefill(**kw)) == code
+
+
+def test_bad_enums_and_null_pointers():
+    lib = msa.load_library()
+    p = _prefill()
+    c = p.c()
+    c.dtype = 7
+    assert lib.msa_index_scores(ctypes.byref(c), FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    c = p.c()
+    c.mode = 3
+    assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    c = p.c()
+    c.algo = 9
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_index_scores(None, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    c = p.c()
+    assert lib.msa_index_scores(ctypes.byref(c), 0, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_index_scores(ctypes.byref(c), FAKE + 2, FAKE, FAKE, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+
+
+def test_mode_mismatch_rejected():
+    lib = msa.load_library()
+    c = _prefill().c()
+    assert lib.msa_sparse_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                      0) == msa.MSA_ERR_INVALID_ARGUMENT
+
+
+def _decode(**kw):
+    base = dict(dtype="bf16", mode="decode", num_groups=8, heads_per_group=8, index_dim=128,
+                top_k=16, batch=4, max_len=131072)
+    base.update(kw)
+    p = msa.Problem(**base)
+    c = p.c()
+    c.seq_lens = FAKE
+    return c
+
+
+def test_decode_validation_and_workspace():
+    lib = msa.load_library()
+    n = ctypes.c_size_t(0)
+    c = _decode()
+    assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
+                                  ctypes.byref(n)) == msa.MSA_OK
+    # B * G * top_k splits * Hpg heads * (128 + 2) floats, each part 256-byte aligned
+    units = 4 * 8 * 16 * 8
+    assert n.value == units * 128 * 4 + ((units * 2 * 4 + 255) // 256) * 256
+    # too small a workspace is refused before launching
+    assert lib.msa_sparse_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      n.value - 1, 0) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    bad = _decode()
+    bad.seq_lens = 0
+    assert lib.msa_block_topk(ctypes.byref(bad), FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    for kw in (dict(batch=0), dict(max_len=0), dict(batch=70000)):
+        c = _decode(**kw)
+        assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_workspace_size(ctypes.byref(_decode()), 99, ctypes.byref(n)) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_workspace_size(ctypes.byref(_decode()), 0, None) == msa.MSA_ERR_INVALID_ARGUMENT
+
+
+def test_empty_chunk_is_a_no_op():
+    """q_count == 0 returns MSA_OK without launching (safe without a device)."""
+    lib = msa.load_library()
+    c = _prefill(q_begin=4096, q_count=0).c()
+    assert lib.msa_index_scores(ctypes.byref(c), FAKE, FAKE, FAKE, 0) == msa.MSA_OK
+    assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_OK
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0) \
+        == msa.MSA_OK

@@ -1,0 +1,188 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes are small enough for the oracle to finish in seconds yet span several
+workgroup tiles and ragged tails. Full-size workloads are checked on sampled rows in
+test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_05_amd import msa, synth
+from oracle import msa_oracle as orc
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _to(x, dev=DEV):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+_ORACLE = {}
+
+
+def _oracle_prefill(key, x, top_k, rows=None):
+    """The oracle's result for one case, computed once per test session."""
+    if key not in _ORACLE:
+        _ORACLE[key] = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k, rows=rows)
+    return _ORACLE[key]
+
+
+def _run_prefill(x, top_k, q_begin=0, q_count=None, algo="auto"):
+    xd = _to(x)
+    out = torch.zeros_like(xd["q"])
+    out, idx, bs = msa.prefill(xd, top_k, q_begin=q_begin, q_count=q_count, algo=algo, out=out)
+    torch.cuda.synchronize()
+    return parity.np32(out), idx.cpu().numpy(), parity.np32(bs)
+
+
+PREFILL_CASES = [
+    # T, G, Hpg, d_idx, top_k, dtype, planted
+    (4096, 2, 3, 64, 4, "f32", 0),      # the fp32 correctness workload
+    (1000, 2, 3, 64, 4, "f32", 0),      # ragged tail
+    (1500, 8, 8, 128, 4, "bf16", 3),
+    (2900, 4, 8, 128, 16, "bf16", 4),   # 23 blocks > top_k = 16
+    (700, 1, 16, 128, 2, "bf16", 0),    # one group, 16 heads per group
+    (640, 3, 1, 64, 3, "bf16", 0),      # one head per group, G = 3
+]
+
+
+@pytest.mark.parametrize("algo", ["query_centric", "auto"])
+@pytest.mark.parametrize("T,G,Hpg,d_idx,top_k,dtype,planted", PREFILL_CASES)
+def test_prefill_parity(T, G, Hpg, d_idx, top_k, dtype, planted, algo):
+    x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype=dtype, seed=T + G, planted_per_group=planted)
+    print(f"prefill parity T={T} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k} {dtype} {algo}", flush=True)
+    out, idx, bs = _run_prefill(x, top_k, algo=algo)
+    res = _oracle_prefill((T, G, Hpg, d_idx, top_k, dtype, planted), x, top_k)
+    info = parity.check_prefill(x, np.arange(T), out, idx, bs, res, top_k, label=f"T={T}")
+    print(info)
+
+
+@pytest.mark.parametrize("algo", ["query_centric", "auto"])
+def test_prefill_chunked_rows(algo):
+    """q_begin/q_count: a chunk in the middle of the sequence gives the same rows."""
+    T, G, Hpg, top_k = 1500, 4, 8, 4
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=77, planted_per_group=2)
+    q0, qn = 700, 600
+    out, idx, bs = _run_prefill(x, top_k, q_begin=q0, q_count=qn, algo=algo)
+    rows = np.arange(q0, q0 + qn)
+    res = _oracle_prefill("chunk", x, top_k, rows=rows)
+    parity.check_prefill(x, rows, out, idx, bs, res, top_k, q_begin=q0, label="chunk")
+    assert np.all(out[:q0] == 0) and np.all(out[q0 + qn:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_all_blocks_equals_dense(dtype):
+    """top_k >= number of blocks: sparse prefill == the oracle's dense causal attention,
+    and the dense GQA entry point gives the same."""
+    T, G, Hpg = 777, 2, 4
+    x = synth.prefill_inputs(T, G, Hpg, 128, 64, dtype=dtype, seed=5)
+    out, idx, _ = _run_prefill(x, 64)
+    ref = orc.dense_prefill(x["q"], x["k"], x["v"])
+    tol = parity.OUT_TOL[x["q"].dtype]
+    assert np.max(np.abs(out - ref)) <= tol
+    for t in range(T):
+        b = t // 128
+        assert idx[t, 0].tolist() == list(range(b + 1)) + [-1] * (64 - b - 1)
+    xd = _to(x)
+    p = msa.Problem(dtype=dtype, mode="prefill", num_groups=G, heads_per_group=Hpg, index_dim=64,
+                    top_k=1, seq_len=T, q_begin=0, q_count=T)
+    dense = torch.zeros_like(xd["q"])
+    msa.msa_dense_gqa_attn(p, xd["q"], xd["k"], xd["v"], dense)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(parity.np32(dense) - ref)) <= tol
+
+
+def _run_decode(x, top_k):
+    xd = _to(x)
+    out, idx, bs = msa.decode(xd, top_k)
+    torch.cuda.synchronize()
+    return parity.np32(out), idx.cpu().numpy(), parity.np32(bs)
+
+
+DECODE_CASES = [
+    # B, max_len, seq_lens, G, Hpg, d_idx, top_k, dtype, planted
+    (3, 3000, [3000, 1, 1537], 8, 8, 128, 4, "bf16", 0),
+    (2, 4000, [4000, 2900], 8, 8, 128, 16, "bf16", 16),
+    (2, 2000, [2000, 1280], 2, 3, 64, 4, "f32", 0),
+    (4, 1000, [1000, 999, 129, 128], 4, 16, 128, 3, "bf16", 2),
+]
+
+
+@pytest.mark.parametrize("B,max_len,lens,G,Hpg,d_idx,top_k,dtype,planted", DECODE_CASES)
+def test_decode_parity(B, max_len, lens, G, Hpg, d_idx, top_k, dtype, planted):
+    x = synth.decode_inputs(B, max_len, G, Hpg, 128, d_idx, dtype=dtype, seed=B + max_len,
+                            planted_per_group=planted, seq_lens=lens)
+    print(f"decode parity B={B} L={lens} G={G} Hpg={Hpg} k={top_k} {dtype}", flush=True)
+    out, idx, bs = _run_decode(x, top_k)
+    res = orc.decode(x["q"], x["k_cache"], x["v_cache"], x["q_idx"], x["k_idx"], x["seq_lens"], top_k)
+    print(parity.check_decode(x, out, idx, bs, res, top_k, label="decode"))
+
+
+def test_decode_equals_last_prefill_row():
+    """The same tokens as a prefill and as a decode cache: the decode step reproduces
+    the last prefill row's selection, and its output to within rounding."""
+    T, G, Hpg, top_k = 2000, 4, 8, 4
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=21, planted_per_group=2)
+    out_p, idx_p, _ = _run_prefill(x, top_k)
+    xdec = dict(q=x["q"][T - 1][None].contiguous(), k_cache=x["k"][None].contiguous(),
+                v_cache=x["v"][None].contiguous(), q_idx=x["q_idx"][T - 1][None].contiguous(),
+                k_idx=x["k_idx"][None].contiguous(), seq_lens=torch.tensor([T], dtype=torch.int32))
+    out_d, idx_d, _ = _run_decode(xdec, top_k)
+    assert np.array_equal(idx_p[T - 1], idx_d[0])
+    assert np.max(np.abs(out_p[T - 1] - out_d[0])) <= 2e-2
+
+
+def test_dense_decode_entry():
+    B, L, G, Hpg = 3, 2500, 4, 8
+    x = synth.decode_inputs(B, L, G, Hpg, 128, 128, dtype="bf16", seed=8, seq_lens=[2500, 700, 1])
+    xd = _to(x)
+    p = msa.decode_problem(xd, 4)
+    ws = msa.alloc_workspace(p, "dense_gqa_attn")
+    out = torch.zeros_like(xd["q"])
+    msa.msa_dense_gqa_attn(p, xd["q"], xd["k_cache"], xd["v_cache"], out, ws)
+    torch.cuda.synchronize()
+    ref = orc.dense_decode(x["q"], x["k_cache"], x["v_cache"], x["seq_lens"])
+    assert np.max(np.abs(parity.np32(out) - ref)) <= 2e-2
+
+
+def test_repeat_runs_bit_identical():
+    """No atomics on any output path: two runs give identical bits."""
+    T, G, Hpg, top_k = 1500, 8, 8, 4
+    x = _to(synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=3, planted_per_group=2))
+    a = [t.clone() for t in msa.prefill(x, top_k)]
+    b = [t.clone() for t in msa.prefill(x, top_k)]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    xdd = _to(synth.decode_inputs(2, 3000, 8, 8, 128, 128, dtype="bf16", seed=4))
+    a = [t.clone() for t in msa.decode(xdd, 16)]
+    b = [t.clone() for t in msa.decode(xdd, 16)]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_topk_handles_ties_and_minus_zero_on_device():
+    """Crafted block-score rows through msa_block_topk (no index kernel): exact ties,
+    -0.0 vs +0.0, a row whose candidates overflow the LDS buffer (all equal)."""
+    G, top_k, T = 1, 4, 128 * 700
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=1, index_dim=128,
+                    top_k=top_k, seq_len=T, q_begin=T - 3, q_count=3)
+    nblk = p.nblk
+    b = (T - 1) // 128
+    s = torch.zeros((3, G, nblk), dtype=torch.float32)
+    s[0, 0, :b] = torch.arange(b, dtype=torch.float32) % 7       # many exact ties at 6
+    s[1, 0, :b] = 0.0
+    s[1, 0, 1:b:2] = -0.0                                           # all zero: lowest ids win
+    s[2, 0, :b] = 1.0                                               # all equal: overflow path
+    s[2, 0, 650] = 2.0
+    idx = torch.empty((3, G, top_k), dtype=torch.int32, device=DEV)
+    msa.msa_block_topk(p, s.to(DEV), idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(3):
+        sel, _ = orc.select_blocks(s[r, 0, :b].double().numpy(), b, top_k)
+        assert got[r, 0].tolist() == sel.tolist(), r
