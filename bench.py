@@ -1,0 +1,443 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X (gfx950).
+
+Default run (N = 1):
+  * headline: causal MSA prefill of one 131072-token sequence, bf16, 8 KV heads x 8
+    query heads per group, head_dim 128, index dim 128, 128-token blocks, top_k 16
+    (index scores -> top-k -> sparse attention, timed as one step);
+  * decode: one MSA decode step of 8 sequences against 1,048,576-token bf16 caches with
+    the same heads (index scan -> top-k -> split-K sparse attention + combine).
+Each is timed with HIP events on the stream the kernels run on, after W untimed
+warmup steps; the dominant kernel of each is also timed launch by launch for its
+roofline fraction. The CPU oracle is then timed on a bounded sample of the same
+inputs (and the sampled rows are checked against the GPU result).
+
+One JSON line goes to stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA prefill tok/s @128K & decode µs/tok @1M; % MFMA peak / % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+BLOCK = 128
+
+WORKLOADS = {
+    "prefill_128k": dict(kind="prefill", T=131072, G=8, Hpg=8, d_idx=128, top_k=16, planted=8,
+                         dtype="bf16", chunk=131072),
+    "prefill_1m": dict(kind="prefill", T=1 << 20, G=8, Hpg=8, d_idx=128, top_k=16, planted=16,
+                       dtype="bf16", chunk=131072),
+    "prefill_4k_f32": dict(kind="prefill", T=4096, G=2, Hpg=3, d_idx=64, top_k=4, planted=0,
+                           dtype="f32", chunk=4096),
+    "decode_1m": dict(kind="decode", B=8, L=1 << 20, G=8, Hpg=8, d_idx=128, top_k=16, planted=16,
+                      dtype="bf16"),
+    "decode_128k": dict(kind="decode", B=4, L=131072, G=8, Hpg=8, d_idx=128, top_k=16,
+                        planted=16, dtype="bf16"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work (what the method must do; not the dense work it avoids) ---------
+
+def prefill_index_flops(T, G, d_idx, top_k):
+    nblk = (T + BLOCK - 1) // BLOCK
+    s = sum(b for b in range(top_k, nblk))
+    # rows of local block b score b full blocks, only when b >= top_k
+    tokens_per_block = [min(BLOCK, T - b * BLOCK) for b in range(nblk)]
+    return sum(2.0 * d_idx * G * BLOCK * b * tokens_per_block[b] for b in range(top_k, nblk))
+
+
+def prefill_attn_flops(T, Hq, D, top_k):
+    tot = 0
+    for t_block in range((T + BLOCK - 1) // BLOCK):
+        n_in = min(BLOCK, T - t_block * BLOCK)
+        kept = min(top_k, t_block + 1) - 1           # full non-local blocks
+        # sum over the block's tokens of visible keys: 128*kept + (t mod 128) + 1
+        tot += n_in * BLOCK * kept + n_in * (n_in + 1) // 2
+    return 4.0 * D * Hq * tot
+
+
+def decode_bytes(lens, G, Hpg, D, d_idx, top_k, esize):
+    tot = 0
+    for L in lens:
+        b = (L - 1) // BLOCK
+        scan = b * BLOCK if b >= top_k else 0
+        if b + 1 <= top_k:
+            n = L
+        else:
+            n = BLOCK * (top_k - 1) + (L - 1) % BLOCK + 1
+        tot += scan * d_idx * esize + 2 * esize * D * G * n + esize * (2 * G * Hpg * D + G * d_idx)
+    return tot
+
+
+def decode_scan_bytes(lens, d_idx, top_k, esize):
+    tot = 0
+    for L in lens:
+        b = (L - 1) // BLOCK
+        if b >= top_k:
+            tot += b * BLOCK * d_idx * esize
+    return tot
+
+
+# ---- timing helpers -----------------------------------------------------------------------
+
+class KernelTimer:
+    """HIP events around one entry point's launches, on the stream they run on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        s = self.torch.cuda.current_stream()
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.a.record(s)
+        return self
+
+    def __exit__(self, *exc):
+        s = self.torch.cuda.current_stream()
+        b = self.torch.cuda.Event(enable_timing=True)
+        b.record(s)
+        self.pairs.append((self.a, b))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+# ---- prefill --------------------------------------------------------------------------------
+
+def run_prefill(name, cfg, args, torch, msa, synth):
+    T, G, Hpg, d_idx, top_k = cfg["T"], cfg["G"], cfg["Hpg"], cfg["d_idx"], cfg["top_k"]
+    chunk = min(cfg["chunk"], T)
+    log(f"[{name}] generating inputs T={T} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k}")
+    x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype=cfg["dtype"], seed=1000 + T,
+                             planted_per_group=cfg["planted"], device="cuda")
+    torch.cuda.synchronize()
+    q = x["q"]
+    out = torch.empty_like(q)
+    chunks = [(c0, min(chunk, T - c0)) for c0 in range(0, T, chunk)]
+    probs = [msa.Problem(dtype=cfg["dtype"], mode="prefill", num_groups=G, heads_per_group=Hpg,
+                         index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n,
+                         algo=args.algo) for c0, n in chunks]
+    bs = torch.empty((chunk, G, probs[0].nblk), dtype=torch.float32, device="cuda")
+    idx_full = torch.empty((T, G, top_k), dtype=torch.int32, device="cuda")
+    ws_bytes = max(msa.msa_workspace_size(p, "sparse_attn_prefill") for p in probs)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
+
+    timers = {}
+
+    def step(timed):
+        for p, (c0, n) in zip(probs, chunks):
+            idx = idx_full[c0:c0 + n]
+            if not timed:
+                msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+                msa.msa_block_topk(p, bs, idx)
+                msa.msa_sparse_attn_prefill(p, q, x["k"], x["v"], idx, out, ws)
+                continue
+            with timers.setdefault("index_scores", KernelTimer(torch)):
+                msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+            with timers.setdefault("block_topk", KernelTimer(torch)):
+                msa.msa_block_topk(p, bs, idx)
+            with timers.setdefault("sparse_attn", KernelTimer(torch)):
+                msa.msa_sparse_attn_prefill(p, q, x["k"], x["v"], idx, out, ws)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    # the step time, with nothing between the launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        step(False)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    # per-kernel durations: events around every launch of each entry point
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    per_kernel = {k: v.mean_ms() * len(chunks) for k, v in timers.items()}
+
+    idx_flops = prefill_index_flops(T, G, d_idx, top_k)
+    att_flops = prefill_attn_flops(T, G * Hpg, 128, top_k)
+    peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    idx_ms_launch = timers["index_scores"].mean_ms()
+    idx_tflops = idx_flops / len(chunks) / (idx_ms_launch * 1e-3) / 1e12
+    total_tflops = (idx_flops + att_flops) / (ms * 1e-3) / 1e12
+    res = dict(
+        workload=name, T=T, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
+        chunk=chunk, algo=args.algo, ms_per_step=ms, wall_s=wall, tok_per_s=T / (ms * 1e-3),
+        kernel_ms_per_step=per_kernel,
+        flops=dict(index=idx_flops, attention=att_flops),
+        path_tflops=total_tflops, path_frac_of_peak=total_tflops / peak,
+        roofline=dict(bound="mfma", kernel="index_scores_prefill", achieved=idx_tflops,
+                      peak=peak, unit="TFLOP/s", frac=idx_tflops / peak, traffic=None,
+                      work_per_launch=idx_flops / len(chunks), launch_ms=idx_ms_launch),
+    )
+    log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
+        f"path {total_tflops:.1f} TFLOP/s ({res['path_frac_of_peak']*100:.1f}% of peak)  "
+        f"index {idx_tflops:.1f} TFLOP/s")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"], res["parity"] = prefill_oracle_sample(name, cfg, x, out, idx_full,
+                                                                   args)
+    del x, out, bs, idx_full, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_oracle_sample(name, cfg, x, out, idx_full, args):
+    """Time the oracle on 32-token slices of evenly spaced query blocks until about
+    args.cpu_seconds have passed, and compare those rows with the GPU's."""
+    import numpy as np
+    from oracle import msa_oracle as orc
+    from tests import parity
+
+    T, top_k = cfg["T"], cfg["top_k"]
+    host = {k: x[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+    nblk = (T + BLOCK - 1) // BLOCK
+    order = np.linspace(nblk - 1, 0, num=min(nblk, 64)).astype(int)
+    done, secs, worst, ties, differ, nsl = 0, 0.0, 0.0, 0, 0, 0
+    for j, b in enumerate(order):
+        lo = int(b) * BLOCK + (j % 4) * 32
+        rows = np.arange(lo, min(lo + 32, T))
+        if len(rows) == 0:
+            continue
+        t0 = time.perf_counter()
+        res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], top_k,
+                          rows=rows)
+        secs += time.perf_counter() - t0
+        done += len(rows)
+        nsl += 1
+        got_out = out[rows[0]:rows[-1] + 1].float().cpu().numpy()
+        got_idx = idx_full[rows[0]:rows[-1] + 1].cpu().numpy()
+        info = parity.check_prefill(host, rows, got_out, got_idx, None, res, top_k,
+                                    q_begin=int(rows[0]), out_offset=int(rows[0]), label=name)
+        worst = max(worst, info["err"])
+        ties += info["near_ties"]
+        differ += info["differ"]
+        if secs >= args.cpu_seconds:
+            break
+    cores = blas_threads()
+    base = dict(value=done / secs, unit="tok/s", cores=cores, kind="oracle",
+                sample=f"{done} query tokens x {cfg['G']} groups in {nsl} slices of 32 tokens "
+                       f"from evenly spaced query blocks of the same {T}-token input, latest "
+                       f"first (whole rows: index scores over all earlier keys, top-k, "
+                       f"attention)",
+                seconds=secs, cpu=cpu_model())
+    par = dict(rows_checked=done, max_abs_err=worst, near_tie_rows=ties,
+               near_tie_selection_differences=differ, ok=True)
+    log(f"[{name}] oracle {base['value']:.3g} tok/s on {cores} threads; parity {par}")
+    return base, par
+
+
+# ---- decode ------------------------------------------------------------------------------
+
+def run_decode(name, cfg, args, torch, msa, synth):
+    B, L, G, Hpg, d_idx, top_k = cfg["B"], cfg["L"], cfg["G"], cfg["Hpg"], cfg["d_idx"], cfg["top_k"]
+    log(f"[{name}] generating inputs B={B} L={L} G={G} Hpg={Hpg} k={top_k}")
+    x = synth.decode_inputs(B, L, G, Hpg, 128, d_idx, dtype=cfg["dtype"], seed=2000 + B,
+                            planted_per_group=cfg["planted"], device="cuda")
+    torch.cuda.synchronize()
+    p = msa.decode_problem(x, top_k)
+    out = torch.empty_like(x["q"])
+    bs = msa.alloc_block_scores(p)
+    idx = msa.alloc_block_idx(p)
+    ws = msa.alloc_workspace(p, "sparse_attn_decode")
+
+    timers = {}
+
+    def step(timed):
+        if not timed:
+            msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+            msa.msa_block_topk(p, bs, idx)
+            msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx, out, ws)
+            return
+        with timers.setdefault("index_scan", KernelTimer(torch)):
+            msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+        with timers.setdefault("block_topk", KernelTimer(torch)):
+            msa.msa_block_topk(p, bs, idx)
+        with timers.setdefault("sparse_attn", KernelTimer(torch)):
+            msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx, out, ws)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(args.steps):
+        step(True)
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    # untimed-by-kernel loop: the step time without per-kernel events in between
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(s)
+    for _ in range(args.steps):
+        step(False)
+    e3.record(s)
+    torch.cuda.synchronize()
+    ms_plain = e2.elapsed_time(e3) / args.steps
+    lens = [L] * B
+    esize = 2 if cfg["dtype"] == "bf16" else 4
+    tot_bytes = decode_bytes(lens, G, Hpg, 128, d_idx, top_k, esize)
+    scan_bytes = decode_scan_bytes(lens, d_idx, top_k, esize)
+    scan_ms = timers["index_scan"].mean_ms()
+    scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
+    res = dict(
+        workload=name, B=B, L=L, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
+        us_per_step=ms_plain * 1e3, us_per_token=ms_plain * 1e3 / B,
+        us_per_step_with_kernel_events=ms * 1e3, wall_s=wall,
+        kernel_us={k: v.mean_ms() * 1e3 for k, v in timers.items()},
+        bytes_per_step=tot_bytes, path_gbs=tot_bytes / (ms_plain * 1e-3) / 1e9,
+        path_frac_of_hbm=tot_bytes / (ms_plain * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        roofline=dict(bound="hbm", kernel="index_scores_decode", achieved=scan_gbs,
+                      peak=PEAK_HBM_GBS, unit="GB/s", frac=scan_gbs / PEAK_HBM_GBS,
+                      traffic=None, work_per_launch=scan_bytes, launch_ms=scan_ms),
+    )
+    log(f"[{name}] {res['us_per_step']:.1f} us/step {res['us_per_token']:.2f} us/token  "
+        f"kernels {res['kernel_us']}  path {res['path_gbs']:.0f} GB/s "
+        f"({res['path_frac_of_hbm']*100:.1f}% of HBM)  scan {scan_gbs:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"], res["parity"] = decode_oracle_sample(name, cfg, x, out, idx, args,
+                                                                  torch)
+    del x, out, bs, idx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_oracle_sample(name, cfg, x, out, idx, args, torch):
+    import numpy as np
+    from oracle import msa_oracle as orc
+    from tests import parity
+
+    B, top_k = cfg["B"], cfg["top_k"]
+    done, secs, worst, ties, differ = 0, 0.0, 0.0, 0, 0
+    for b in range(B):
+        hx = {k: x[k][b:b + 1].cpu() for k in ("q", "q_idx", "k_idx", "seq_lens")}
+        hx["k_cache"] = x["k_cache"][b:b + 1].cpu()
+        hx["v_cache"] = x["v_cache"][b:b + 1].cpu()
+        t0 = time.perf_counter()
+        res = orc.decode(hx["q"], hx["k_cache"], hx["v_cache"], hx["q_idx"], hx["k_idx"],
+                         hx["seq_lens"], top_k)
+        secs += time.perf_counter() - t0
+        done += 1
+        info = parity.check_decode(hx, out[b:b + 1].float().cpu().numpy(),
+                                   idx[b:b + 1].cpu().numpy(), None, res, top_k, label=name)
+        worst = max(worst, info["err"])
+        ties += info["near_ties"]
+        differ += info["differ"]
+        del hx
+        if secs >= args.cpu_seconds:
+            break
+    cores = blas_threads()
+    base = dict(value=secs / done * 1e6, unit="us/token", cores=cores, kind="oracle",
+                sample=f"{done} of the {B} sequences of the same decode step (whole rows: index "
+                       f"scan over all {cfg['L']} cached keys, top-k, attention)",
+                seconds=secs, cpu=cpu_model())
+    par = dict(sequences_checked=done, max_abs_err=worst, near_tie_rows=ties,
+               near_tie_selection_differences=differ, ok=True)
+    log(f"[{name}] oracle {base['value']:.4g} us/token on {cores} threads; parity {par}")
+    return base, par
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill", default="prefill_128k", help="prefill workload ('none' to skip)")
+    ap.add_argument("--decode", default="decode_1m", help="decode workload ('none' to skip)")
+    ap.add_argument("--algo", default="auto", choices=["auto", "query_centric", "kv_centric"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MSA hot path here has no multi-GPU "
+              "path (no sharding, no collectives). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_05_amd import msa, synth
+    msa.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    pre = dec = None
+    if args.prefill != "none":
+        pre = run_prefill(args.prefill, WORKLOADS[args.prefill], args, torch, msa, synth)
+    if args.decode != "none":
+        dec = run_decode(args.decode, WORKLOADS[args.decode], args, torch, msa, synth)
+
+    head = pre if pre is not None else dec
+    if pre is not None:
+        value, unit, hib, ms = pre["tok_per_s"], "tok/s", True, pre["ms_per_step"]
+        config = {"workload": f"MSA causal prefill, 1 sequence x {pre['T']} tokens, {pre['dtype']}, "
+                              f"{pre['G']} KV heads x {pre['Hpg']} q heads/group, head_dim 128, "
+                              f"index dim {pre['d_idx']}, block 128, top_k {pre['top_k']}",
+                  "name": pre["workload"], "global_batch": 1, "seq_len": pre["T"],
+                  "parallelism": "single GPU"}
+    else:
+        value, unit, hib, ms = dec["us_per_token"], "us/token", False, dec["us_per_step"] / 1e3
+        config = {"workload": f"MSA decode step, batch {dec['B']}, cache {dec['L']} tokens",
+                  "name": dec["workload"], "global_batch": dec["B"], "seq_len": dec["L"],
+                  "parallelism": "single GPU"}
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": hib, "scaling": "weak",
+        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic (seeded; see DESIGN.md)",
+        "config": config, "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+    }
+    if pre is not None:
+        line["prefill"] = pre
+    if dec is not None:
+        line["decode"] = dec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

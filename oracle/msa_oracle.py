@@ -33,8 +33,8 @@ design notes of the repository):
   R9 attention scale 1 / sqrt(head_dim);
   R11 decode: a cache of L tokens holds the current token, whose position is L - 1.
 
-The inputs may be NumPy arrays or torch tensors (fp32 / bf16); they are widened
-exactly to float64 first.
+The inputs may be NumPy arrays or torch tensors (fp32 / bf16); each slice a row
+uses is widened exactly to float64 when it is used.
 """
 
 from __future__ import annotations
@@ -47,14 +47,50 @@ BLOCK = 128
 NEAR_TIE_REL = 1e-5
 
 
-def as_f64(x) -> np.ndarray:
-    """Exact widening of fp32 / bf16 / fp64 data (NumPy or torch) to float64."""
-    if hasattr(x, "detach"):  # torch tensor; bf16 -> fp32 is exact
+class BF16Bits:
+    """bf16 data held as its raw 16-bit patterns (a NumPy uint16 array), so that slicing
+    stays in NumPy and widening is exact: the pattern is the top half of an fp32."""
+
+    def __init__(self, bits: np.ndarray):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, i):
+        return BF16Bits(self.bits[i])
+
+    def __len__(self):
+        return len(self.bits)
+
+
+def host(x):
+    """Zero-copy NumPy view of an input (torch CPU tensor or NumPy array)."""
+    if hasattr(x, "detach"):  # torch tensor
         import torch
-        x = x.detach().to("cpu")
-        if x.dtype != torch.float64:
-            x = x.to(torch.float32)
-        x = x.numpy()
+        x = x.detach()
+        if x.device.type != "cpu":
+            x = x.cpu()
+        if x.dtype == torch.bfloat16:
+            return BF16Bits(x.view(torch.int16).numpy().view(np.uint16))
+        return x.numpy()
+    return x
+
+
+_WIDEN_AT_ENTRY = 1 << 24  # inputs up to this many elements are widened once, up front
+
+
+def host_small_f64(x):
+    """host(x), already widened to float64 when it is small."""
+    x = host(x)
+    n = int(np.prod(x.shape)) if len(x.shape) else 1
+    return as_f64(x) if n <= _WIDEN_AT_ENTRY else x
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact widening of fp32 / bf16 / fp64 data to float64."""
+    if hasattr(x, "detach"):
+        x = host(x)
+    if isinstance(x, BF16Bits):
+        return (x.bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
 
 
@@ -119,15 +155,18 @@ def visible_keys(sel, t: int, block: int = BLOCK) -> np.ndarray:
 
 
 def _row(q_t, k_g, v_g, q_idx_tg, k_idx, t, top_k, block, scale, bs=None):
+    """One (query, group): selection and attention. K/V rows are widened to float64
+    only for the tokens the selection reaches."""
     b = t // block
     if b + 1 <= top_k:
         sel, tie = np.arange(b + 1, dtype=np.int64), False
     else:
         if bs is None:
-            bs = index_block_scores(q_idx_tg[None, :], k_idx, b, block)[0]
+            bs = index_block_scores(as_f64(q_idx_tg)[None, :], as_f64(k_idx[: b * block]), b,
+                                    block)[0]
         sel, tie = select_blocks(bs, b, top_k)
     j = visible_keys(sel, t, block)
-    return attend(q_t, k_g[j], v_g[j], scale), sel, tie, bs
+    return attend(as_f64(q_t), as_f64(k_g[j]), as_f64(v_g[j]), scale), sel, tie, bs
 
 
 def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) -> dict:
@@ -136,9 +175,10 @@ def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) ->
     q [T, G*Hpg, D]; k, v [G, T, D]; q_idx [T, G, d_idx]; k_idx [T, d_idx].
     Returns dict(out [R, Hq, D], sel [R][G] -> ascending ids, near_tie [R, G] bool,
     block_scores {(i, g): array of b scores} for rows that were scored, rows [R]).
+    Inputs are widened to float64 slice by slice, as each row needs them.
     """
-    q, k, v = as_f64(q), as_f64(k), as_f64(v)
-    q_idx, k_idx = as_f64(q_idx), as_f64(k_idx)
+    q, k, v = host_small_f64(q), host_small_f64(k), host_small_f64(v)
+    q_idx, k_idx = host_small_f64(q_idx), host_small_f64(k_idx)
     T, Hq, D = q.shape
     G = k.shape[0]
     Hpg = Hq // G
@@ -156,8 +196,9 @@ def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) ->
     for b, idxs in by_block.items():
         bs_rows = None
         if b + 1 > top_k:
-            qi = q_idx[rows[idxs]].reshape(len(idxs) * G, -1)
-            bs_rows = index_block_scores(qi, k_idx, b, block).reshape(len(idxs), G, b)
+            qi = as_f64(q_idx[rows[idxs]]).reshape(len(idxs) * G, -1)
+            bs_rows = index_block_scores(qi, as_f64(k_idx[: b * block]), b, block)
+            bs_rows = bs_rows.reshape(len(idxs), G, b)
         for n, i in enumerate(idxs):
             t = int(rows[i])
             for g in range(G):
@@ -180,11 +221,11 @@ def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
     q [B, G*Hpg, D]; k_cache, v_cache [B, G, Lmax, D]; q_idx [B, G, d_idx];
     k_idx [B, Lmax, d_idx]; seq_lens [B]. The query sits at position L_b - 1 (R11).
     """
-    q, kc, vc = as_f64(q), as_f64(k_cache), as_f64(v_cache)
-    q_idx, k_idx = as_f64(q_idx), as_f64(k_idx)
     lens = [int(x) for x in np.asarray(as_f64(seq_lens)).tolist()]
+    q, k_cache, v_cache = host_small_f64(q), host_small_f64(k_cache), host_small_f64(v_cache)
+    q_idx, k_idx = host_small_f64(q_idx), host_small_f64(k_idx)
     B, Hq, D = q.shape
-    G = kc.shape[1]
+    G = k_cache.shape[1]
     Hpg = Hq // G
     scale = 1.0 / math.sqrt(D)
     out = np.zeros((B, Hq, D))
@@ -193,10 +234,16 @@ def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
     scores = {}
     for bi in range(B):
         t = lens[bi] - 1
+        b = t // block
+        bs_all = None
+        if b + 1 > top_k:                        # all G index queries in one product
+            bs_all = index_block_scores(as_f64(q_idx[bi]), as_f64(k_idx[bi][: b * block]), b,
+                                        block)
         for g in range(G):
             hs = slice(g * Hpg, (g + 1) * Hpg)
-            o, sel, tg, bs = _row(q[bi, hs], kc[bi, g], vc[bi, g], q_idx[bi, g], k_idx[bi],
-                                  t, top_k, block, scale)
+            bs = None if bs_all is None else bs_all[g]
+            o, sel, tg, bs = _row(q[bi, hs], k_cache[bi, g], v_cache[bi, g], q_idx[bi, g],
+                                  k_idx[bi], t, top_k, block, scale, bs)
             out[bi, hs] = o
             sel_all[bi][g] = sel
             tie[bi, g] = tg
@@ -261,7 +308,7 @@ def selection_array(sel, top_k: int) -> np.ndarray:
 def attend_on_selection(q_t, k_g, v_g, sel, t, block: int = BLOCK) -> np.ndarray:
     """Attention of one token's group heads over a given selection (for rows where
     a device picked a different set on a declared near tie)."""
-    q_t, k_g, v_g = as_f64(q_t), as_f64(k_g), as_f64(v_g)
+    q_t, k_g, v_g = as_f64(q_t), host(k_g), host(v_g)
     sel = [int(c) for c in sel if int(c) >= 0]
     j = visible_keys(sel, t, block)
-    return attend(q_t, k_g[j], v_g[j], 1.0 / math.sqrt(q_t.shape[-1]))
+    return attend(q_t, as_f64(k_g[j]), as_f64(v_g[j]), 1.0 / math.sqrt(q_t.shape[-1]))

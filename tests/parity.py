@@ -44,8 +44,10 @@ def check_selection(idx_gpu, oracle_sel, near_tie, top_k, label=""):
     return {tuple(x) for x in np.argwhere(diff).tolist()}
 
 
-def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, label=""):
-    """Compare a prefill run for oracle rows `rows` (absolute token ids)."""
+def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, out_offset=0,
+                  label=""):
+    """Compare a prefill run for oracle rows `rows` (absolute token ids). idx_gpu and
+    bs_gpu start at row q_begin, out_gpu at row out_offset."""
     dtype = x["q"].dtype
     tol = OUT_TOL[dtype]
     G = x["k"].shape[0]
@@ -55,7 +57,7 @@ def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, labe
     differ = check_selection(idx_rows, res["sel"], res["near_tie"], top_k, label)
     if bs_gpu is not None:
         check_block_scores(bs_gpu, res["block_scores"], lambda i: rows[i] - q_begin, label)
-    got = out_gpu[rows].astype(np.float64)
+    got = out_gpu[rows - out_offset].astype(np.float64)
     ref = res["out"].copy()
     for (i, g) in differ:
         t = int(rows[i])

@@ -45,7 +45,7 @@ PREFILL_CASES = [
     (4096, 2, 3, 64, 4, "f32", 0),      # the fp32 correctness workload
     (1000, 2, 3, 64, 4, "f32", 0),      # ragged tail
     (1500, 8, 8, 128, 4, "bf16", 3),
-    (2900, 4, 8, 128, 16, "bf16", 4),   # 23 blocks > top_k = 16
+    (2300, 4, 8, 128, 16, "bf16", 4),   # 18 blocks > top_k = 16
     (700, 1, 16, 128, 2, "bf16", 0),    # one group, 16 heads per group
     (640, 3, 1, 64, 3, "bf16", 0),      # one head per group, G = 3
 ]
