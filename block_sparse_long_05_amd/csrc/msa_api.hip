@@ -72,6 +72,11 @@ size_t decode_ws_bytes(const msa_problem* p, bool dense) {
   return align_up(units * MSA_HEAD_DIM * sizeof(float)) + align_up(units * 2 * sizeof(float));
 }
 
+size_t prefill_kv_ws_bytes(const msa_problem* p) {
+  return kv_workspace_bytes(p->dtype == MSA_DTYPE_BF16, p->q_count, p->num_groups,
+                            p->heads_per_group, p->top_k, (int)nblk_of(p));
+}
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -139,6 +144,7 @@ msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes
       return MSA_OK;
     case MSA_ENTRY_SPARSE_ATTN_PREFILL:
       if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
+      if (p->algo != MSA_ALGO_QUERY_CENTRIC) *bytes = prefill_kv_ws_bytes(p);
       return MSA_OK;
     case MSA_ENTRY_SPARSE_ATTN_DECODE:
       if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
@@ -192,9 +198,24 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out))
     return MSA_ERR_INVALID_ARGUMENT;
-  (void)workspace;
-  (void)workspace_bytes;
   if (p->q_count == 0) return MSA_OK;
+  // KV-centric when asked for, or by default when the caller's workspace can hold it.
+  bool kv = p->algo == MSA_ALGO_KV_CENTRIC;
+  if (p->algo != MSA_ALGO_QUERY_CENTRIC) {
+    const size_t need = prefill_kv_ws_bytes(p);
+    const bool fits = workspace != nullptr && workspace_bytes >= need;
+    if (kv && !fits) return workspace == nullptr && workspace_bytes >= need
+                                ? MSA_ERR_INVALID_ARGUMENT
+                                : MSA_ERR_WORKSPACE_TOO_SMALL;
+    kv = fits;
+  }
+  if (kv) {
+    if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_kv_prefill(p->dtype == MSA_DTYPE_BF16, q, k, v, block_idx, out,
+                                        workspace, p->num_groups, p->heads_per_group, p->top_k,
+                                        p->q_begin, p->q_count, p->seq_len, (int)nblk_of(p),
+                                        as_stream(stream)));
+  }
   GatherParams gp = {};
   gp.mode = kPrefillSparse;
   gp.bf16 = p->dtype == MSA_DTYPE_BF16;

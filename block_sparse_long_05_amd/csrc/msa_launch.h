@@ -50,4 +50,12 @@ hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);
 hipError_t launch_decode_combine(int bf16, const float* part_o, const float* part_ml, void* out,
                                  int B, int G, int Hpg, int nsplit, hipStream_t stream);
 
+// KV-centric sparse prefill attention (attn_tile.hip): reverse index, per-block tiles,
+// log-sum-exp merge. `workspace` must hold kv_workspace_bytes(...) bytes.
+size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, int nblk);
+hipError_t launch_kv_prefill(int bf16, const void* q, const void* k, const void* v,
+                             const int32_t* block_idx, void* out, void* workspace, int G, int Hpg,
+                             int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,
+                             int nblk, hipStream_t stream);
+
 }  // namespace msa
