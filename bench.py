@@ -143,7 +143,7 @@ def cpu_model():
 
 def run_prefill(name, cfg, args, torch, msa, synth):
     T, G, Hpg, d_idx, top_k = cfg["T"], cfg["G"], cfg["Hpg"], cfg["d_idx"], cfg["top_k"]
-    chunk = min(cfg["chunk"], T)
+    chunk = min(args.chunk or cfg["chunk"], T)
     log(f"[{name}] generating inputs T={T} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k}")
     x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype=cfg["dtype"], seed=1000 + T,
                              planted_per_group=cfg["planted"], device="cuda")
@@ -389,6 +389,8 @@ def main():
     ap.add_argument("--prefill", default="prefill_128k", help="prefill workload ('none' to skip)")
     ap.add_argument("--decode", default="decode_1m", help="decode workload ('none' to skip)")
     ap.add_argument("--algo", default="auto", choices=["auto", "query_centric", "kv_centric"])
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="prefill query rows per call (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
