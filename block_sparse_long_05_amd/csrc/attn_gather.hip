@@ -74,6 +74,7 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
   const elem *kbase, *vbase, *qrow;
   int64_t limit;  // keys j < limit are visible
   int jbeg, jend; // range of list positions (sparse) or block ids (dense)
+  int koff = 0, kspan = kBlock;  // keys [koff, koff + kspan) of each block
   const int32_t* list = nullptr;
   int64_t bseq = 0, i = 0;
   int g;
@@ -107,8 +108,15 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
     qrow = (const elem*)p.q + (bseq * Hq + (int64_t)g * Hpg) * kHeadDim;
     const int nlist = sparse ? p.top_k : (int)((L - 1) / kBlock) + 1;
     if (sparse) list = p.block_idx + bg * p.top_k;
-    jbeg = sp * p.blocks_per_split;
-    jend = min(jbeg + p.blocks_per_split, nlist);
+    if (p.half_blocks) {
+      jbeg = sp >> 1;
+      jend = min(jbeg + 1, nlist);
+      koff = (sp & 1) * (kBlock / 2);
+      kspan = kBlock / 2;
+    } else {
+      jbeg = sp * p.blocks_per_split;
+      jend = min(jbeg + p.blocks_per_split, nlist);
+    }
   }
   const int blocal = (int)((limit - 1) / kBlock);
   const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
@@ -129,19 +137,35 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
   for (int jj = jbeg; jj < jend; ++jj) {
     const int c = list ? list[jj] : jj;
     if (c < 0 || c > blocal) continue;
-    const int64_t key0 = (int64_t)c * kBlock;
-    const int nvalid = (int)min((int64_t)kBlock, limit - key0);
+    const int64_t key0 = (int64_t)c * kBlock + koff;
+    const int nvalid = (int)min((int64_t)kspan, limit - key0);
+    if (nvalid <= 0) continue;
 
-    // S^T = K . Q^T for 8 tiles of 16 keys.
+    // Half-block (64-key) bf16 units issue their V rows together with the K rows, so
+    // the wave pays one memory round trip for both.
+    constexpr bool kPreV = E::is_bf16;
+    uint32_t vpre[kPreV ? 64 : 1];
+    if constexpr (kPreV) {
+      if (kspan == 64) {
+        const elem* vp0 = vbase + key0 * kHeadDim + 2 * lane;
+#pragma unroll
+        for (int j = 0; j < 64; ++j)
+          vpre[j] = j < nvalid ? *reinterpret_cast<const uint32_t*>(vp0 + (int64_t)j * kHeadDim) : 0u;
+      }
+    }
+    // S^T = K . Q^T for the 16-key tiles (8 per block, 4 per half block).
     f32x4 s4[8];
+    const int ntiles = kspan / 16;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      const int kk = 16 * kt + hcol;
-      const bool ok = kk < nvalid;
-      const elem* kp = kbase + (key0 + (ok ? kk : 0)) * kHeadDim + kgrp * E::kPerLane;
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (kt < ntiles) {
+        const int kk = 16 * kt + hcol;
+        const bool ok = kk < nvalid;
+        const elem* kp = kbase + (key0 + (ok ? kk : 0)) * kHeadDim + kgrp * E::kPerLane;
 #pragma unroll
-      for (int s = 0; s < kNStep; ++s) a = mfma16(ok ? O::load(kp + s * O::kStep) : O::zero(), qop[s], a);
+        for (int s = 0; s < kNStep; ++s) a = mfma16(ok ? O::load(kp + s * O::kStep) : O::zero(), qop[s], a);
+      }
       s4[kt] = a;
     }
     // Scale, mask, block max per head.
@@ -157,14 +181,14 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
       }
     mloc = wave_max_xor(mloc, 16);
     const float m_new = fmaxf(m_run, mloc);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 pv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = m_new == -INFINITY ? 0.f : exp2f(s4[kt][r] - m_new);
+        const float e = m_new == -INFINITY ? 0.f : fast_exp2(s4[kt][r] - m_new);
         pv[r] = e;
         psum += e;
       }
@@ -183,18 +207,40 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
       acc[h][0] *= a;
       acc[h][1] *= a;
     }
-    const elem* vp = vbase + key0 * kHeadDim + 2 * lane;
-    for (int j = 0; j < nvalid; j += 4) {
-      float2 vv[4];
+    if (kPreV && kspan == 64) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        vv[q] = (j + q < nvalid) ? O::load2(vp + (int64_t)(j + q) * kHeadDim) : make_float2(0.f, 0.f);
+      for (int j4 = 0; j4 < 64; j4 += 4) {
+        float2 vv[4];
 #pragma unroll
-      for (int h = 0; h < HMAX; ++h) {
-        if (h < Hpg) {
-          const f32x4 pp = *reinterpret_cast<const f32x4*>(&Ps[h * kPRow + j]);
-          acc[h][0] += pp[0] * vv[0].x + pp[1] * vv[1].x + pp[2] * vv[2].x + pp[3] * vv[3].x;
-          acc[h][1] += pp[0] * vv[0].y + pp[1] * vv[1].y + pp[2] * vv[2].y + pp[3] * vv[3].y;
+        for (int q = 0; q < 4; ++q)
+          vv[q] = make_float2(bf16_bits_to_f32(vpre[j4 + q] & 0xffffu), bf16_bits_to_f32(vpre[j4 + q] >> 16));
+#pragma unroll
+        for (int h = 0; h < HMAX; ++h) {
+          if (h < Hpg) {
+            const f32x4 pp = *reinterpret_cast<const f32x4*>(&Ps[h * kPRow + j4]);
+            acc[h][0] += pp[0] * vv[0].x + pp[1] * vv[1].x + pp[2] * vv[2].x + pp[3] * vv[3].x;
+            acc[h][1] += pp[0] * vv[0].y + pp[1] * vv[1].y + pp[2] * vv[2].y + pp[3] * vv[3].y;
+          }
+        }
+      }
+    } else {
+      const elem* vp = vbase + key0 * kHeadDim + 2 * lane;
+      // V rows in batches of 16 so that many loads are in flight per wave.
+      for (int j0 = 0; j0 < nvalid; j0 += 16) {
+        float2 vv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          vv[q] = (j0 + q < nvalid) ? O::load2(vp + (int64_t)(j0 + q) * kHeadDim) : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int q4 = 0; q4 < 16; q4 += 4) {
+#pragma unroll
+          for (int h = 0; h < HMAX; ++h) {
+            if (h < Hpg) {
+              const f32x4 pp = *reinterpret_cast<const f32x4*>(&Ps[h * kPRow + j0 + q4]);
+              acc[h][0] += pp[0] * vv[q4].x + pp[1] * vv[q4 + 1].x + pp[2] * vv[q4 + 2].x + pp[3] * vv[q4 + 3].x;
+              acc[h][1] += pp[0] * vv[q4].y + pp[1] * vv[q4 + 1].y + pp[2] * vv[q4 + 2].y + pp[3] * vv[q4 + 3].y;
+            }
+          }
         }
       }
     }
@@ -224,6 +270,10 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
   }
 }
 
+// One wave per (sequence, head). Lanes hold the (m, l) of 64 splits at a time (all
+// loaded at once): pass 1 reduces the global max, pass 2 forms each split's weight in
+// its lane and broadcasts it while every lane streams its two dims of the partials,
+// 8 splits in flight. The order of the sum is fixed, so the result is deterministic.
 template <class E>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
@@ -232,18 +282,32 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   const int lane = threadIdx.x;
   const int64_t bg = blockIdx.x / Hpg;
   const int h = blockIdx.x % Hpg;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[((bg * nsplit + sp) * Hpg + h) * 2]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int sp = s0 + lane;
+    if (sp < nsplit) M = fmaxf(M, ml[(bg * nsplit + sp) * Hpg + h].x);
+  }
+  M = wave_max_xor(M, 1);
   float a0 = 0.f, a1 = 0.f, L = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const int64_t idx = (bg * nsplit + sp) * Hpg + h;
-    const float m = part_ml[idx * 2];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
-    L += w * part_ml[idx * 2 + 1];
-    const float2 o = *reinterpret_cast<const float2*>(part_o + idx * kHeadDim + 2 * lane);
-    a0 += w * o.x;
-    a1 += w * o.y;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int sp = s0 + lane;
+    float w = 0.f, l = 0.f;
+    if (sp < nsplit) {
+      const float2 v = ml[(bg * nsplit + sp) * Hpg + h];
+      w = (v.x == -INFINITY) ? 0.f : fast_exp2(v.x - M);
+      l = v.y;
+    }
+    L += wave_sum_xor(w * l, 1);
+    const int cnt = min(64, nsplit - s0);
+#pragma unroll 8
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      const float2 o = *reinterpret_cast<const float2*>(
+          part_o + ((bg * nsplit + s0 + k) * Hpg + h) * kHeadDim + 2 * lane);
+      a0 += wk * o.x;
+      a1 += wk * o.y;
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   KOp<E>::store2(out + (bg * Hpg + h) * kHeadDim + 2 * lane, a0 * inv, a1 * inv);

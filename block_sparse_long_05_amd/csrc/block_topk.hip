@@ -26,19 +26,71 @@ constexpr int kCandCap = 512;
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
 // Steps 3-4 over n items get(i) -> (key, block id), items in ascending block order.
+// Counting uses popcount(ballot(...)) (one scalar op per 64 items) rather than
+// shuffle reductions; up to 64 * kHeldSel items are read once into registers.
+constexpr int kHeldSel = 8;
+
 template <class Get>
 __device__ __forceinline__ void select_exact(Get get, int n, int K, int32_t* out, int lane) {
+  if (n <= 64 * kHeldSel) {
+    uint32_t key[kHeldSel];
+    int32_t idx[kHeldSel];
+#pragma unroll
+    for (int j = 0; j < kHeldSel; ++j) {
+      const int i = 64 * j + lane;
+      uint2 e = make_uint2(0u, 0u);
+      if (i < n) e = get(i);
+      key[j] = e.x;
+      idx[j] = (int32_t)e.y;
+    }
+    const int nj = (n + 63) / 64;
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kHeldSel; ++j)
+        if (j < nj) cnt += __popcll(__ballot(64 * j + lane < n && key[j] >= cand));
+      if (cnt >= K) tau = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < kHeldSel; ++j)
+      if (j < nj) gt += __popcll(__ballot(64 * j + lane < n && key[j] > tau));
+    const int need_eq = K - gt;
+    int eq_base = 0, sel_base = 0;
+#pragma unroll
+    for (int j = 0; j < kHeldSel; ++j) {
+      if (j < nj) {
+        const bool valid = 64 * j + lane < n;
+        const bool is_gt = valid && key[j] > tau;
+        const bool is_eq = valid && key[j] == tau;
+        const uint64_t eqm = __ballot(is_eq);
+        const int eq_rank = eq_base + __popcll(eqm & lanemask_lt(lane));
+        const bool sel = is_gt || (is_eq && eq_rank < need_eq);
+        const uint64_t selm = __ballot(sel);
+        if (sel) out[sel_base + __popcll(selm & lanemask_lt(lane))] = idx[j];
+        eq_base += __popcll(eqm);
+        sel_base += __popcll(selm);
+      }
+    }
+    return;
+  }
   uint32_t tau = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int cnt = 0;
-    for (int i = lane; i < n; i += 64) cnt += get(i).x >= cand ? 1 : 0;
-    cnt = wave_sum_int(cnt);
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      cnt += __popcll(__ballot(i < n && get(i).x >= cand));
+    }
     if (cnt >= K) tau = cand;
   }
   int gt = 0;
-  for (int i = lane; i < n; i += 64) gt += get(i).x > tau ? 1 : 0;
-  gt = wave_sum_int(gt);
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    gt += __popcll(__ballot(i < n && get(i).x > tau));
+  }
   const int need_eq = K - gt;
   int eq_base = 0, sel_base = 0;
   for (int i0 = 0; i0 < n; i0 += 64) {
@@ -122,9 +174,152 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
   }
 }
 
+// Long rows (decode: every cache block is a candidate): one workgroup of 16 waves per
+// row. Wave w takes the exact top-K of its contiguous segment of blocks; because any
+// block of the row's top-K is in the top-K of its own segment under the same order,
+// wave 0 then finishes with an exact selection over the <= 16*K segment winners,
+// which lie in ascending block order segment after segment.
+constexpr int kLongWaves = 16;
+
+__global__ __launch_bounds__(64 * kLongWaves) void block_topk_long_kernel(
+    const float* __restrict__ scores, int32_t* __restrict__ out, int G, int nblk, int top_k,
+    int decode, int64_t q_begin, const int32_t* __restrict__ seq_lens, int64_t max_len) {
+  __shared__ uint32_t win_key[kLongWaves * 64];
+  __shared__ int32_t win_idx[kLongWaves * 64];
+  __shared__ int32_t win_n[kLongWaves];
+  __shared__ uint32_t seg_key[kLongWaves][kCandCap];
+  __shared__ int32_t seg_idx[kLongWaves][kCandCap];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  int b;
+  if (decode) {
+    int64_t L = seq_lens[row / G];
+    L = L < 1 ? 1 : (L > max_len ? max_len : L);
+    b = (int)((L - 1) / kBlock);
+  } else {
+    b = (int)((q_begin + row / G) / kBlock);
+  }
+  int32_t* o = out + row * top_k;
+  if (b + 1 <= top_k) {
+    if (wave == 0)
+      for (int i = lane; i < top_k; i += 64) o[i] = i <= b ? i : -1;
+    return;
+  }
+  const int K = top_k - 1;
+  if (wave == 0 && lane == 0) o[K] = b;
+  if (K == 0) return;
+  const float* s = scores + row * (int64_t)nblk;
+  // segment of this wave: [lo, hi), 64-aligned
+  const int per = ((b + kLongWaves - 1) / kLongWaves + 63) / 64 * 64;
+  const int lo = min(b, wave * per), hi = min(b, lo + per);
+  const int n = hi - lo;
+  int32_t* wi = &win_idx[wave * 64];
+  uint32_t* wk = &win_key[wave * 64];
+  if (n <= K) {  // the whole segment goes through
+    for (int i = lane; i < n; i += 64) {
+      wi[i] = lo + i;
+      wk[i] = ordered_key(s[lo + i]);
+    }
+    if (lane == 0) win_n[wave] = n;
+  } else {
+    // lower bound from lane maxima, candidates to LDS, exact selection. Segments of up
+    // to 64 * kHeld blocks keep each lane's keys in registers (loaded once).
+    constexpr int kHeld = 16;
+    uint32_t held[kHeld];
+    const bool in_regs = n <= 64 * kHeld;
+    uint32_t lmax = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j) {
+        const int c = lo + 64 * j + lane;
+        held[j] = c < hi ? ordered_key(s[c]) : 0u;
+        lmax = max(lmax, held[j]);
+      }
+    } else {
+      for (int c = lo + lane; c < hi; c += 64) lmax = max(lmax, ordered_key(s[c]));
+    }
+    uint32_t lb = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = lb | (1u << bit);
+      if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
+    }
+    uint32_t* ck = seg_key[wave];
+    int32_t* ci = seg_idx[wave];
+    int nc = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j) {
+        const int c = lo + 64 * j + lane;
+        const bool take = c < hi && held[j] >= lb;
+        const uint64_t m = __ballot(take);
+        const int pos = nc + __popcll(m & lanemask_lt(lane));
+        if (take && pos < kCandCap) {
+          ck[pos] = held[j];
+          ci[pos] = c;
+        }
+        nc += __popcll(m);
+      }
+    } else {
+      for (int c0 = lo; c0 < hi; c0 += 64) {
+        const int c = c0 + lane;
+        uint32_t key = 0;
+        if (c < hi) key = ordered_key(s[c]);
+        const bool take = c < hi && key >= lb;
+        const uint64_t m = __ballot(take);
+        const int pos = nc + __popcll(m & lanemask_lt(lane));
+        if (take && pos < kCandCap) {
+          ck[pos] = key;
+          ci[pos] = c;
+        }
+        nc += __popcll(m);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (nc <= kCandCap)
+      select_exact([&](int i) { return make_uint2(ck[i], (uint32_t)ci[i]); }, nc, K, wi, lane);
+    else
+      select_exact([&](int i) { return make_uint2(ordered_key(s[lo + i]), (uint32_t)(lo + i)); }, n,
+                   K, wi, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < K; i += 64) wk[i] = ordered_key(s[wi[i]]);
+    if (lane == 0) win_n[wave] = K;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // Concatenate the winners (ascending block order; at most 16 * 63 of them, stored
+  // flat over the segment buffers) and select exactly.
+  uint32_t* all_key = &seg_key[0][0];
+  int32_t* all_idx = &seg_idx[0][0];
+  int tot = 0;
+  for (int w = 0; w < kLongWaves; ++w) {
+    const int m = win_n[w];
+    for (int i = lane; i < m; i += 64) {
+      all_key[tot + i] = win_key[w * 64 + i];
+      all_idx[tot + i] = win_idx[w * 64 + i];
+    }
+    tot += m;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  select_exact([&](int i) { return make_uint2(all_key[i], (uint32_t)all_idx[i]); }, tot, K, o,
+               lane);
+}
+
 hipError_t launch_block_topk(const float* block_scores, int32_t* block_idx, int64_t rows, int G,
                              int nblk, int top_k, int decode, int64_t q_begin,
                              const int32_t* seq_lens, int64_t max_len, hipStream_t stream) {
+  if (nblk > 2048 && rows <= 8192) {
+    hipLaunchKernelGGL(block_topk_long_kernel, dim3((unsigned)rows), dim3(64 * kLongWaves), 0,
+                       stream, block_scores, block_idx, G, nblk, top_k, decode, q_begin, seq_lens,
+                       max_len);
+    return hipGetLastError();
+  }
   const int64_t grid = (rows + kTopkWaves - 1) / kTopkWaves;
   hipLaunchKernelGGL(block_topk_kernel, dim3((unsigned)grid), dim3(64 * kTopkWaves), 0, stream,
                      block_scores, block_idx, rows, G, nblk, top_k, decode, q_begin, seq_lens,

@@ -217,6 +217,107 @@ __global__ __launch_bounds__(256) void index_scores_decode_kernel(
   }
 }
 
+// Decode, bf16 with index dim 128 and up to 16 groups: each wave streams its blocks
+// through a private ring of 4 LDS stages of 32 keys (8 KiB each) filled by direct
+// global->LDS loads, with three stages in flight while one is consumed. A quarter-wave
+// loads one whole 256-byte key row, so the reads are fully coalesced; the 16-byte
+// chunks of row r are stored XOR-swizzled (position p holds chunk p ^ (r % 16)), so
+// the MFMA operand reads - 16 rows, one chunk each per quarter-wave - fall in distinct
+// LDS banks.
+constexpr int kScanKeys = 32;                     // keys per stage
+constexpr int kScanStage = kScanKeys * 256;       // bytes per stage (bf16, d = 128)
+constexpr int kScanRing = 4;                      // stages per wave
+constexpr int kScanLoads = kScanKeys / 4;         // 1 KiB loads per stage
+
+__device__ __forceinline__ void scan_issue_stage(const uint16_t* rows, uint8_t* stage_lds,
+                                                 int lane) {
+  // load i covers key rows 4i .. 4i+3 of the stage
+#pragma unroll
+  for (int i = 0; i < kScanLoads; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const int p = lane & 15;
+    const int chunk = p ^ (r & 15);
+    const uint16_t* src = rows + (int64_t)r * 128 + chunk * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)src, (__attribute__((address_space(3))) void*)(stage_lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding).
+#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
+__global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    float* __restrict__ block_scores, const int32_t* __restrict__ seq_lens, int64_t max_len,
+    int G, int top_k, int nblk, int blocks_per_wg) {
+  __shared__ __align__(16) uint8_t lds[4][kScanRing][kScanStage];  // 128 KiB
+  constexpr int kPerBlock = kBlock / kScanKeys;                      // stages per block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  int64_t L = seq_lens[b];
+  L = L < 1 ? 1 : (L > max_len ? max_len : L);
+  const int bl = (int)((L - 1) / kBlock);
+  if (bl < top_k) return;
+  const int c0 = blockIdx.x * blocks_per_wg;
+  if (c0 >= bl) return;
+  const int c1 = min(c0 + blocks_per_wg, bl);
+  const uint16_t* kbase = k_idx + (int64_t)b * max_len * 128;
+  const int gq = lane & 15;
+  const int q = lane >> 4;
+  u32x4 qop[4];
+  {
+    const bool ok = gq < G;
+    const uint16_t* qp = q_idx + ((int64_t)b * G + (ok ? gq : 0)) * 128 + 8 * q;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qop[s] = ok ? *reinterpret_cast<const u32x4*>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // This wave's blocks c0 + wave, c0 + wave + 4, ...: stages (block, quarter) in order.
+  const int nb = (c1 - (c0 + wave) + 3) / 4;
+  const int nstages = nb > 0 ? kPerBlock * nb : 0;
+  auto stage_rows = [&](int st) {
+    const int c = c0 + wave + 4 * (st / kPerBlock);
+    return kbase + ((int64_t)c * kBlock + (st % kPerBlock) * kScanKeys) * 128;
+  };
+  for (int st = 0; st < kScanRing - 1 && st < nstages; ++st)
+    scan_issue_stage(stage_rows(st), lds[wave][st], lane);
+  float mx = -INFINITY;
+  for (int st = 0; st < nstages; ++st) {
+    if (st + kScanRing - 1 < nstages)
+      scan_issue_stage(stage_rows(st + kScanRing - 1), lds[wave][(st + kScanRing - 1) % kScanRing], lane);
+    // stages issued after this one: min(3, nstages - 1 - st); wait until only those remain
+    const int later = min(kScanRing - 1, nstages - 1 - st);
+    if (later >= 3) MSA_WAIT_VMCNT(3 * kScanLoads);
+    else if (later == 2) MSA_WAIT_VMCNT(2 * kScanLoads);
+    else if (later == 1) MSA_WAIT_VMCNT(kScanLoads);
+    else MSA_WAIT_VMCNT(0);
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* sl = lds[wave][st % kScanRing];
+#pragma unroll
+    for (int kt = 0; kt < kScanKeys / 16; ++kt) {
+      const int m = 16 * kt + (lane & 15);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int pos = (4 * s + q) ^ (m & 15);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sl + m * 256 + pos * 16);
+        acc = mfma16(a, qop[s], acc);
+      }
+      mx = fmaxf(mx, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+    }
+    // this buffer's reads are done before it is refilled kScanRing - 1 stages on
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (st % kPerBlock == kPerBlock - 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const int c = c0 + wave + 4 * (st / kPerBlock);
+      if (lane < 16 && gq < G) block_scores[((int64_t)b * G + gq) * nblk + c] = mx;
+      mx = -INFINITY;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------
@@ -263,6 +364,14 @@ static hipError_t launch_decode_t(const void* q_idx, const void* k_idx, float* b
   per = per < 4 ? 4 : (per > 64 ? 64 : per);
   per = (per + 3) / 4 * 4;
   const int gx = (int)((nblk + per - 1) / per);
+  if constexpr (E::is_bf16 && DI == 128) {
+    if (G <= 16) {
+      hipLaunchKernelGGL(index_scores_decode_lds_kernel, dim3(gx, B), dim3(256), 0, st,
+                         (const uint16_t*)q_idx, (const uint16_t*)k_idx, bs, seq_lens, max_len, G,
+                         top_k, nblk, (int)per);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((index_scores_decode_kernel<E, DI>), dim3(gx, B), dim3(256), 0, st,
                      (const typename E::elem*)q_idx, (const typename E::elem*)k_idx, bs, seq_lens,
                      max_len, G, top_k, nblk, (int)per);

@@ -50,11 +50,11 @@ int64_t nblk_of(const msa_problem* p) {
   return ceil_div(p->mode == MSA_MODE_PREFILL ? p->seq_len : p->max_len, MSA_BLOCK_SIZE);
 }
 
-// Decode split-K plan: sparse uses one kept block per split; dense spreads the cache
-// blocks so that the launch has a few thousand waves.
+// Decode split-K plan: sparse uses one half (64 keys) of one kept block per split;
+// dense spreads the cache blocks so that the launch has a few thousand waves.
 void decode_split(const msa_problem* p, bool dense, int* nsplit, int* bps) {
   if (!dense) {
-    *nsplit = p->top_k;
+    *nsplit = 2 * p->top_k;
     *bps = 1;
     return;
   }
@@ -110,6 +110,7 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
   gp.max_len = p->max_len;
   gp.nsplit = nsplit;
   gp.blocks_per_split = bps;
+  gp.half_blocks = dense ? 0 : 1;
   hipError_t e = launch_gather_attn(gp, st);
   if (e != hipSuccess) return MSA_ERR_HIP;
   return hip_status(launch_decode_combine(gp.bf16, part_o, part_ml, out, p->batch, p->num_groups,

@@ -42,6 +42,7 @@ struct GatherParams {
   int64_t max_len;
   int nsplit;            // decode: splits per (sequence, group)
   int blocks_per_split;  // decode
+  int half_blocks;       // decode: each split covers one half (64 keys) of one listed block
 };
 
 hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);

@@ -116,8 +116,9 @@ def test_decode_validation_and_workspace():
     c = _decode()
     assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
                                   ctypes.byref(n)) == msa.MSA_OK
-    # B * G * top_k splits * Hpg heads * (128 + 2) floats, each part 256-byte aligned
-    units = 4 * 8 * 16 * 8
+    # B * G * (2 * top_k half-block splits) * Hpg heads * (128 + 2) floats, each part
+    # 256-byte aligned
+    units = 4 * 8 * 32 * 8
     assert n.value == units * 128 * 4 + ((units * 2 * 4 + 255) // 256) * 256
     # too small a workspace is refused before launching
     assert lib.msa_sparse_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,

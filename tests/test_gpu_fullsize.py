@@ -1,0 +1,62 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times, on outputs the oracle can compute one by one (sampled query rows / sequences).
+
+Workloads: decode of 4 sequences x 131072 cached tokens (all rows checked), decode of
+8 x 1,048,576 (two sequences checked), causal prefill of 131072 tokens (sampled
+32-token slices). All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
+index dim 128, 128-token blocks, top_k 16, planted blocks as in the benchmark.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_05_amd import msa, synth
+from oracle import msa_oracle as orc
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(B, L, seed, check):
+    x = synth.decode_inputs(B, L, 8, 8, 128, 128, dtype="bf16", seed=seed, planted_per_group=16,
+                            device="cuda")
+    out, idx, _ = msa.decode(x, 16)
+    torch.cuda.synchronize()
+    print(f"decode B={B} L={L} ran", flush=True)
+    for b in check:
+        hx = {k: x[k][b:b + 1].cpu() for k in ("q", "q_idx", "k_idx", "seq_lens", "k_cache",
+                                               "v_cache")}
+        res = orc.decode(hx["q"], hx["k_cache"], hx["v_cache"], hx["q_idx"], hx["k_idx"],
+                         hx["seq_lens"], 16)
+        info = parity.check_decode(hx, out[b:b + 1].float().cpu().numpy(),
+                                   idx[b:b + 1].cpu().numpy(), None, res, 16, label=f"seq {b}")
+        print(b, info, flush=True)
+        del hx
+
+
+def test_decode_128k_all_sequences():
+    _decode_case(4, 131072, seed=2004, check=range(4))
+
+
+def test_decode_1m_sampled_sequences():
+    _decode_case(8, 1 << 20, seed=2008, check=[0, 7])
+
+
+def test_prefill_128k_sampled_rows():
+    T = 131072
+    x = synth.prefill_inputs(T, 8, 8, 128, 128, dtype="bf16", seed=1000 + T,
+                             planted_per_group=8, device="cuda")
+    out, idx, _ = msa.prefill(x, 16)
+    torch.cuda.synchronize()
+    host = {k: x[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+    for lo in (0, 2048 + 17, 65536 - 16, T - 32):
+        rows = np.arange(lo, min(lo + 32, T))
+        res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], 16,
+                          rows=rows)
+        got_out = out[rows[0]:rows[-1] + 1].float().cpu().numpy()
+        got_idx = idx[rows[0]:rows[-1] + 1].cpu().numpy()
+        info = parity.check_prefill(host, rows, got_out, got_idx, None, res, 16,
+                                    q_begin=int(rows[0]), out_offset=int(rows[0]),
+                                    label=f"rows {lo}")
+        print(lo, info, flush=True)

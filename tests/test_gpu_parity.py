@@ -186,3 +186,33 @@ def test_topk_handles_ties_and_minus_zero_on_device():
     for r in range(3):
         sel, _ = orc.select_blocks(s[r, 0, :b].double().numpy(), b, top_k)
         assert got[r, 0].tolist() == sel.tolist(), r
+
+
+def test_topk_long_rows_decode():
+    """Decode rows with more than 2048 blocks take the workgroup-per-row selection:
+    random scores, exact ties, -0.0/+0.0, an all-equal row (candidate overflow) and a
+    row whose last segment is shorter than top_k."""
+    G, top_k = 2, 16
+    max_len = 128 * 5000
+    lens = [max_len, 300000, 128 * 2049 + 5]
+    nblk = (max_len + 127) // 128
+    gen = torch.Generator().manual_seed(5)
+    s = torch.randn((3, G, nblk), generator=gen, dtype=torch.float32)
+    s[1, 0] = (torch.arange(nblk) % 5).float()                    # ties at the top value 4
+    s[1, 1] = 0.0
+    s[1, 1, 1::2] = -0.0
+    s[2, 0] = 1.0                                                  # all equal: overflow path
+    s[2, 0, 1000] = 3.0
+    s[2, 1, :2040] = -5.0                                          # winners in the short tail
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    p = msa.Problem(dtype="bf16", mode="decode", num_groups=G, heads_per_group=1, index_dim=128,
+                    top_k=top_k, batch=3, max_len=max_len, seq_lens=seq)
+    idx = torch.empty((3, G, top_k), dtype=torch.int32, device=DEV)
+    msa.msa_block_topk(p, s.to(DEV), idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(3):
+        blocal = (lens[b] - 1) // 128
+        for g in range(G):
+            sel, _ = orc.select_blocks(s[b, g, :blocal].double().numpy(), blocal, top_k)
+            assert got[b, g].tolist() == sel.tolist(), (b, g)
