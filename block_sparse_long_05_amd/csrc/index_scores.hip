@@ -19,6 +19,9 @@
 
 namespace msa {
 
+// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding).
+#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
 template <class E>
 struct Operand;
 template <>
@@ -154,6 +157,126 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_kernel(
   }
 }
 
+// Prefill, bf16: 4 waves x 128 index-query rows (4 row tiles of 32) per workgroup. The
+// key block is staged by direct global->LDS loads into an unpadded, double-buffered
+// LDS block whose 16-byte chunks are XOR-swizzled by row (position p of row r holds
+// chunk p ^ (r % 16)): a quarter-wave loads one whole key row (coalesced) and the MFMA
+// operand reads of 8 rows at a time fall in distinct banks. Each K operand read feeds
+// the 4 row tiles. Block maxima are kept for a few blocks and written together.
+template <int DI>
+struct PrefillLds {
+  static constexpr int kRowBytes = DI * 2;                 // one key row in LDS
+  static constexpr int kChunks = DI / 8;                   // 16-byte chunks per row
+  static constexpr int kBufBytes = kBlock * kRowBytes;     // one staged block
+  static constexpr int kLoadsPerWave = kBufBytes / 1024 / 4;
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;    // rows one 1 KiB load covers
+  static constexpr int kSteps = DI / 16;                   // 32x32x16 k-steps
+};
+
+template <int DI>
+__device__ __forceinline__ void prefill_issue_block(const uint16_t* k_idx, int c, uint8_t* buf,
+                                                    int wave, int lane) {
+  typedef PrefillLds<DI> C;
+  const uint16_t* src0 = k_idx + (int64_t)c * kBlock * DI;
+#pragma unroll
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    const int li = wave * C::kLoadsPerWave + i;            // 1 KiB load index in the block
+    const int r = li * C::kRowsPerLoad + lane / C::kChunks;
+    const int p = lane % C::kChunks;
+    const int chunk = p ^ (r & (C::kChunks - 1));
+    __builtin_amdgcn_global_load_lds((const void*)(src0 + (int64_t)r * DI + chunk * 8),
+                                     (__attribute__((address_space(3))) void*)(buf + li * 1024),
+                                     16, 0, 0);
+  }
+}
+
+template <int DI>
+__global__ __launch_bounds__(256, 2) void index_scores_prefill_lds_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    float* __restrict__ block_scores, int64_t q_begin, int64_t q_count, int G, int top_k,
+    int nblk) {
+  typedef PrefillLds<DI> C;
+  __shared__ __align__(16) uint8_t lds[2][C::kBufBytes];
+  constexpr int kRows = 512;  // rows per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t nrows = q_count * G;
+  const int64_t r0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * kRows;  // heaviest rows first
+  const int64_t r_last = min(r0 + kRows - 1, nrows - 1);
+  const int cmax = (int)((q_begin + r_last / G) / kBlock);
+  if (cmax < top_k) return;
+
+  // B operands: 4 row tiles of 32 rows; lane group q holds dims 16s + 8q .. +8.
+  const int q = lane >> 5;
+  u32x4 qop[4][C::kSteps];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t R = r0 + 128 * wave + 32 * rt + (lane & 31);
+    const bool ok = R < nrows;
+    const uint16_t* qp = q_idx + (q_begin * G + (ok ? R : 0)) * DI + 8 * q;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s)
+      qop[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // Rows this lane writes: tiles 2*q and 2*q + 1 at column lane % 32.
+  int64_t Rw[2];
+  int bw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    Rw[j] = r0 + 128 * wave + 32 * (2 * q + j) + (lane & 31);
+    bw[j] = Rw[j] < nrows ? (int)((q_begin + Rw[j] / G) / kBlock) : -1;
+    if (bw[j] < top_k) bw[j] = 0;  // rows keeping all their blocks write nothing
+  }
+
+  prefill_issue_block<DI>(k_idx, 0, lds[0], wave, lane);
+  MSA_WAIT_VMCNT(0);
+  __syncthreads();
+  constexpr int kBatch = DI == 128 ? 4 : 8;  // blocks whose maxima are written together
+  for (int cb = 0; cb < cmax; cb += kBatch) {
+    float outv[2][kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c = cb + j;
+      outv[0][j] = outv[1][j] = 0.f;
+      if (c < cmax) {
+        const bool has_next = c + 1 < cmax;
+        if (has_next) prefill_issue_block<DI>(k_idx, c + 1, lds[(c + 1) & 1], wave, lane);
+        const uint8_t* kb = lds[c & 1];
+        float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int m = 32 * kt + (lane & 31);
+          f32x16 acc[4] = {};
+#pragma unroll
+          for (int s = 0; s < C::kSteps; ++s) {
+            const int pos = (2 * s + q) ^ (m & (C::kChunks - 1));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(kb + m * C::kRowBytes + pos * 16);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(a, qop[rt][s], acc[rt]);
+          }
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx[rt] = fmaxf(mx[rt], fmaxf(acc[rt][r], acc[rt][r + 1]));
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
+        outv[0][j] = q == 0 ? mx[0] : mx[2];
+        outv[1][j] = q == 0 ? mx[1] : mx[3];
+        if (has_next) MSA_WAIT_VMCNT(0);  // this wave's part of block c + 1 has landed
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int rj = 0; rj < 2; ++rj) {
+      float* orow = block_scores + (Rw[rj] < nrows ? Rw[rj] : 0) * (int64_t)nblk;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (cb + j < bw[rj]) orow[cb + j] = outv[rj][j];
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // Decode
 // ------------------------------------------------------------------------------------
@@ -243,8 +366,6 @@ __device__ __forceinline__ void scan_issue_stage(const uint16_t* rows, uint8_t* 
   }
 }
 
-// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding).
-#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
 
 __global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
@@ -327,6 +448,13 @@ static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, float* 
                                    hipStream_t st) {
   typedef PrefillCfg<E, DI> C;
   const int64_t rows = q_count * G;
+  if constexpr (E::is_bf16) {
+    const int64_t grid = (rows + 511) / 512;
+    hipLaunchKernelGGL(index_scores_prefill_lds_kernel<DI>, dim3((unsigned)grid), dim3(256), 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, bs, q_begin, q_count, G,
+                       top_k, nblk);
+    return hipGetLastError();
+  }
   const int64_t grid = (rows + 255) / 256;
   const size_t lds = 2 * C::kBuf * sizeof(typename E::elem);
   hipLaunchKernelGGL((index_scores_prefill_kernel<E, DI>), dim3((unsigned)grid), dim3(256), lds,
