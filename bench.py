@@ -118,6 +118,28 @@ class KernelTimer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
+def measured_traffic(kernel_fragment):
+    """HBM bytes per launch of a kernel from profiles/traffic.json (two rocprofv3 --pmc
+    runs, scaled by a plain copy), or None when absent or when the kernel's source has
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        from block_sparse_long_05_amd.profiling import source_hash
+        t = json.load(open(path))
+        for name, v in t["kernels"].items():
+            if kernel_fragment in name:
+                if v.get("source_hash") != source_hash(name):
+                    return None
+                if v.get("read_bytes") is None or v.get("write_bytes") is None:
+                    return None
+                return v["read_bytes"] + v["write_bytes"]
+    except Exception:
+        return None
+    return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -209,7 +231,8 @@ def run_prefill(name, cfg, args, torch, msa, synth):
         flops=dict(index=idx_flops, attention=att_flops),
         path_tflops=total_tflops, path_frac_of_peak=total_tflops / peak,
         roofline=dict(bound="mfma", kernel="index_scores_prefill", achieved=idx_tflops,
-                      peak=peak, unit="TFLOP/s", frac=idx_tflops / peak, traffic=None,
+                      peak=peak, unit="TFLOP/s", frac=idx_tflops / peak,
+                      traffic=measured_traffic("index_scores_prefill"),
                       work_per_launch=idx_flops / len(chunks), launch_ms=idx_ms_launch),
     )
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
@@ -333,7 +356,7 @@ def run_decode(name, cfg, args, torch, msa, synth):
         path_frac_of_hbm=tot_bytes / (ms_plain * 1e-3) / 1e9 / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", kernel="index_scores_decode", achieved=scan_gbs,
                       peak=PEAK_HBM_GBS, unit="GB/s", frac=scan_gbs / PEAK_HBM_GBS,
-                      traffic=None, work_per_launch=scan_bytes, launch_ms=scan_ms),
+                      traffic=measured_traffic("index_scores_decode"), work_per_launch=scan_bytes, launch_ms=scan_ms),
     )
     log(f"[{name}] {res['us_per_step']:.1f} us/step {res['us_per_token']:.2f} us/token  "
         f"kernels {res['kernel_us']}  path {res['path_gbs']:.0f} GB/s "
@@ -389,6 +412,9 @@ def main():
     ap.add_argument("--prefill", default="prefill_128k", help="prefill workload ('none' to skip)")
     ap.add_argument("--decode", default="decode_1m", help="decode workload ('none' to skip)")
     ap.add_argument("--algo", default="auto", choices=["auto", "query_centric", "kv_centric"])
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (the reference "
+                         "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefill query rows per call (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -407,6 +433,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration_mib:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     pre = dec = None
     if args.prefill != "none":
@@ -414,6 +446,8 @@ def main():
     if args.decode != "none":
         dec = run_decode(args.decode, WORKLOADS[args.decode], args, torch, msa, synth)
 
+    if pre is None and dec is None:
+        return
     head = pre if pre is not None else dec
     if pre is not None:
         value, unit, hib, ms = pre["tok_per_s"], "tok/s", True, pre["ms_per_step"]

@@ -1,0 +1,140 @@
+"""Summaries of rocprofv3 output for the MSA kernels (text for profiles/, and the HBM
+traffic table bench.py reports).
+
+    python -m block_sparse_long_05_amd.profiling stats <kernel_stats.csv> [--cmd "..."]
+    python -m block_sparse_long_05_amd.profiling traffic --fetch <dir> --write <dir>
+            --copy-mib N --out <traffic.json> [--cmd "..."]
+
+`traffic` reads the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then
+WRITE_SIZE, KiB per dispatch) taken with bench.py --copy-calibration-mib N, scales each
+counter by what it reads for that plain N MiB device copy (read and written bytes are
+known exactly), and stores bytes per launch for each MSA kernel together with a hash
+of the kernel's source file.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# kernel-name fragment -> source file that defines it
+KERNEL_SOURCES = {
+    "index_scores_prefill": "index_scores.hip",
+    "index_scores_decode": "index_scores.hip",
+    "block_topk": "block_topk.hip",
+    "kv_": "attn_tile.hip",
+    "gather_attn": "attn_gather.hip",
+    "decode_combine": "attn_gather.hip",
+    "dense_": "attn_dense.hip",
+}
+
+
+def source_hash(kernel_name: str):
+    for frag, src in KERNEL_SOURCES.items():
+        if frag in kernel_name:
+            path = os.path.join(CSRC, src)
+            if os.path.exists(path):
+                return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return None
+
+
+def short_name(name: str) -> str:
+    base = name.split("(")[0].replace("void ", "")
+    return base.strip()
+
+
+def stats_text(stats_csv: str, cmd: str = "") -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["rocprofv3 --kernel-trace --stats: MSA kernels (durations in microseconds)"]
+    if cmd:
+        out.append(f"command: {cmd}")
+    out.append(f"{'calls':>6} {'avg_us':>11} {'min_us':>11} {'max_us':>11}  kernel")
+    for r in rows:
+        if "msa::" not in r["Name"]:
+            continue
+        out.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:11.1f} "
+                   f"{float(r['MinNs']) / 1e3:11.1f} {float(r['MaxNs']) / 1e3:11.1f}  "
+                   f"{short_name(r['Name'])}")
+    return "\n".join(out) + "\n"
+
+
+_per_dispatch = collections.defaultdict(lambda: collections.defaultdict(list))
+
+
+def counter_means(directory: str) -> dict:
+    """{kernel name: {counter: mean value per dispatch}} from a --pmc run's CSVs."""
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r.get("Kernel_Name") or ""
+            ctr = r.get("Counter_Name")
+            if ctr is None:
+                continue
+            agg[name][ctr].append(float(r["Counter_Value"]))
+            _per_dispatch[ctr][name].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+def _copy_value(means: dict, counter: str) -> float:
+    # the runtime's device-to-device copy kernel; the calibration copy is its largest
+    # dispatch in the run
+    vals = [max(v) for name, v in _per_dispatch.get(counter, {}).items() if "copyBuffer" in name]
+    if not vals:
+        raise SystemExit(f"no copy kernel found for {counter}")
+    return max(vals)  # the calibration copy is by far the largest dispatch
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_mib: float, cmd: str = "") -> dict:
+    fm, wm = counter_means(fetch_dir), counter_means(write_dir)
+    copy_bytes = copy_mib * (1 << 20)
+    f_copy = _copy_value(fm, "FETCH_SIZE") * 1024.0
+    w_copy = _copy_value(wm, "WRITE_SIZE") * 1024.0
+    fs, ws = copy_bytes / f_copy, copy_bytes / w_copy
+    kernels = {}
+    for name in sorted(set(fm) | set(wm)):
+        if "msa::" not in name:
+            continue
+        rd = fm.get(name, {}).get("FETCH_SIZE")
+        wr = wm.get(name, {}).get("WRITE_SIZE")
+        kernels[short_name(name)] = dict(
+            read_bytes=None if rd is None else rd * 1024.0 * fs,
+            write_bytes=None if wr is None else wr * 1024.0 * ws,
+            source_hash=source_hash(name))
+    return dict(copy_mib=copy_mib, fetch_scale=fs, write_scale=ws, command=cmd,
+                kernels=kernels)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("--cmd", default="")
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--copy-mib", type=float, required=True)
+    b.add_argument("--out", required=True)
+    b.add_argument("--cmd", default="")
+    args = ap.parse_args()
+    if args.what == "stats":
+        print(stats_text(args.csv, args.cmd), end="")
+    else:
+        t = traffic(args.fetch, args.write, args.copy_mib, args.cmd)
+        with open(args.out, "w") as f:
+            json.dump(t, f, indent=1)
+        for k, v in t["kernels"].items():
+            print(f"{k}: read {v['read_bytes']}, write {v['write_bytes']}")
+        print(f"scale: fetch x{t['fetch_scale']:.3f}, write x{t['write_scale']:.3f}")
+
+
+if __name__ == "__main__":
+    main()
