@@ -1,21 +1,28 @@
-// Main branch of MSA for prefill, KV-centric ("reverse index") form.
+// Main branch of MSA for prefill: a hybrid of query-tile and KV-centric ("reverse index")
+// attention.
 //
 // The researchpapers.dev summary of the MSA paper ("What it means for inference
 // teams") names the real costs of a sparse prefill kernel: index construction, top-k,
 // query gathering, reverse indexing and load balancing; the baguaai.com note on MSA
-// describes the kernel as aggregating queries on the KV side. This file implements
-// that data flow for gfx950:
+// describes the kernel as aggregating queries on the KV side. Neighbouring tokens tend to
+// keep the same blocks (the local block always, blocks that score high for a whole
+// stretch of text often), so the work is split by how widely a block is kept:
 //
-//   1. reverse index: a counting sort of every kept (token, group, slot) entry of
-//      block_idx by its KV block (group g, block c) - count, exclusive scan, scatter;
-//   2. kv_attn_kernel: the sorted entries are cut into fixed tiles of 128 entries
+//   1. kv_classify_kernel: per query tile (a few consecutive tokens) and group, the
+//      blocks kept by at least half of the tile's tokens form the tile's shared list;
+//   2. reverse index of the other ("rare") kept entries: a counting sort by KV block
+//      (group g, block c) - count, exclusive scan, scatter;
+//   3. kv_attn_kernel: the sorted rare entries are cut into fixed tiles of 256 entries
 //      (load balance independent of how popular a block is). Each tile walks its runs
-//      of equal (g, c): the block's K (row-major) and V (transposed) are staged in LDS
-//      once and every query of the run attends to it with 32x32x16 bf16 MFMAs,
-//      rows = (entry, head) pairs gathered from Q. A row sees one block, so its softmax
-//      is exact within the block; it writes a partial (o / l, m, l);
-//   3. kv_merge_kernel: per (token, group) the <= top_k partials are merged with a
-//      log-sum-exp combine in slot order (deterministic; no atomics touch values).
+//      of equal (g, c): the block's K and V (transposed) are staged in LDS once and
+//      every query of the run attends to it with 32x32x16 bf16 MFMAs, rows = (entry,
+//      head) pairs gathered from Q. A row sees one block, so its softmax is exact within
+//      the block; it writes a partial (o / l, m, l);
+//   4. qtile_attn kernels: per (query tile, group) the shared blocks are staged in LDS
+//      one after another and every row of the tile runs an online softmax over those it
+//      keeps (others masked); the row then folds in its rare partials with a
+//      log-sum-exp combine in slot order (deterministic; no atomics touch values) and
+//      writes the output.
 //
 // MFMA orientation: S^T = K . Q^T so that a lane owns one query row and holds 16 of
 // its keys per 32-key tile; the softmax reductions are in-lane plus one exchange
@@ -39,14 +46,78 @@ __global__ void kv_zero_kernel(int32_t* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
+// Partials are stored in fragment order: value d = 32 dt + 8 jj + 4 q + r of a head's 128
+// sits at 64 q + 16 dt + 4 jj + r, so the 64 values one lane holds are contiguous.
+__device__ __forceinline__ int frag_pos(int dt, int jj, int q) { return 64 * q + 16 * dt + 4 * jj; }
+
+// Query tiles: the rows of one 32-row MFMA tile are floor(32 / Hpg) tokens x Hpg heads,
+// and a query tile is the row tiles of one workgroup (4 for bf16, 8 for fp32).
+__host__ __device__ __forceinline__ int qtile_tokens(int Hpg, int bf16) {
+  return (bf16 ? 4 : 8) * (32 / Hpg);
+}
+
+// True when block c is in the tile's shared list (ascending, -1 padded).
+__device__ __forceinline__ bool in_shared(const int32_t* slist, int top_k, int c) {
+  for (int j = 0; j < top_k; ++j) {
+    const int v = slist[j];
+    if (v < 0 || v > c) return false;
+    if (v == c) return true;
+  }
+  return false;
+}
+
+// Bucket (g * nblk + c) of a kept entry that goes through the reverse index, -1 for
+// padding, invisible ids and entries of a shared block of the entry's query tile.
 __device__ __forceinline__ int64_t entry_bucket(const int32_t* block_idx, int64_t id, int G,
-                                                int top_k, int64_t q_begin, int nblk) {
+                                                int top_k, int64_t q_begin, int nblk,
+                                                const int32_t* shared, int QT) {
   const int c = block_idx[id];
   const int64_t rowg = id / top_k;
   const int g = (int)(rowg % G);
-  const int64_t t = q_begin + rowg / G;
+  const int64_t i = rowg / G;
+  const int64_t t = q_begin + i;
   if (c < 0 || (int64_t)c > t / kBlock) return -1;
+  if (in_shared(shared + ((i / QT) * G + g) * top_k, top_k, c)) return -1;
   return (int64_t)g * nblk + c;
+}
+
+// One wave per (query tile, group): a block is shared when at least half of the tile's
+// tokens keep it. Candidates are the blocks of the tile's last token (any block kept by
+// half of the tokens is likely among them; the split only moves work between the two
+// paths, every kept entry is still handled exactly once).
+__global__ __launch_bounds__(256) void kv_classify_kernel(const int32_t* __restrict__ block_idx,
+                                                          int32_t* __restrict__ shared, int G,
+                                                          int top_k, int64_t q_begin,
+                                                          int64_t q_count, int QT, int64_t npairs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= npairs) return;
+  const int64_t tile = pair / G;
+  const int g = (int)(pair % G);
+  const int64_t i0 = tile * QT;
+  const int ntok = (int)min((int64_t)QT, q_count - i0);
+  const int64_t t_last = q_begin + i0 + ntok - 1;
+  int cand = -1;
+  if (lane < top_k) {
+    cand = block_idx[((i0 + ntok - 1) * G + g) * top_k + lane];
+    if (cand < 0 || (int64_t)cand > t_last / kBlock) cand = -1;
+  }
+  int cnt = 0;
+  for (int tok = 0; tok < ntok; ++tok) {
+    const int32_t* tl = block_idx + ((i0 + tok) * G + g) * top_k;
+    const int b = (int)((q_begin + i0 + tok) / kBlock);
+    for (int s = 0; s < top_k; ++s) {
+      const int c = tl[s];
+      cnt += (c >= 0 && c == cand && c <= b) ? 1 : 0;
+    }
+  }
+  const bool keep = cand >= 0 && 2 * cnt >= ntok;
+  const uint64_t m = __ballot(keep);
+  const int pos = __popcll(m & ((1ull << lane) - 1ull));
+  int32_t* out = shared + pair * top_k;
+  if (keep) out[pos] = cand;
+  const int nkeep = __popcll(m);
+  for (int j = nkeep + lane; j < top_k; j += 64) out[j] = -1;
 }
 
 // Popular blocks (the local block, blocks most queries pick) would send every
@@ -57,11 +128,12 @@ __device__ __forceinline__ int64_t entry_bucket(const int32_t* block_idx, int64_
 constexpr int kStripes = 16;
 
 __global__ void kv_count_kernel(const int32_t* __restrict__ block_idx, int64_t n_entries, int G,
-                                int top_k, int64_t q_begin, int nblk, int32_t* __restrict__ count) {
+                                int top_k, int64_t q_begin, int nblk, const int32_t* __restrict__ shared,
+                                int QT, int32_t* __restrict__ count) {
   const int64_t nb = (int64_t)G * nblk;
   for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < n_entries;
        id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = entry_bucket(block_idx, id, G, top_k, q_begin, nblk);
+    const int64_t k = entry_bucket(block_idx, id, G, top_k, q_begin, nblk, shared, QT);
     const int stripe = (int)((id / ((int64_t)G * top_k)) % kStripes);
     if (k >= 0) atomicAdd(&count[stripe * nb + k], 1);
   }
@@ -100,11 +172,12 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict
 
 __global__ void kv_scatter_kernel(const int32_t* __restrict__ block_idx, int64_t n_entries, int G,
                                   int top_k, int64_t q_begin, int nblk,
+                                  const int32_t* __restrict__ shared, int QT,
                                   int32_t* __restrict__ cursor, int32_t* __restrict__ sorted) {
   const int64_t nb = (int64_t)G * nblk;
   for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < n_entries;
        id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = entry_bucket(block_idx, id, G, top_k, q_begin, nblk);
+    const int64_t k = entry_bucket(block_idx, id, G, top_k, q_begin, nblk, shared, QT);
     const int stripe = (int)((id / ((int64_t)G * top_k)) % kStripes);
     if (k >= 0) sorted[atomicAdd(&cursor[stripe * nb + k], 1)] = (int32_t)id;
   }
@@ -213,13 +286,13 @@ struct TileOps<F32> {
 // the K/V block of the next run is loaded into registers while the current run computes
 // and is then written to the other LDS buffer (bf16; fp32 single-buffers), and each
 // wave gathers the queries of its next row tile while the current one finishes.
-template <class E>
+template <class E, int NT = 256>
 struct KvStage {
   typedef typename E::elem elem;
   static constexpr int kPer = 16 / sizeof(elem);                      // elements per chunk
-  static constexpr int kKChunks = kBlock * kHeadDim / kPer / 256;     // K chunks per thread
-  static constexpr int kVItems = E::is_bf16 ? (kBlock / 2) * (kHeadDim / 8) / 256
-                                            : kBlock * (kHeadDim / kPer) / 256;
+  static constexpr int kKChunks = kBlock * kHeadDim / kPer / NT;      // K chunks per thread
+  static constexpr int kVItems = E::is_bf16 ? (kBlock / 2) * (kHeadDim / 8) / NT
+                                            : kBlock * (kHeadDim / kPer) / NT;
   static constexpr int kVRegs = E::is_bf16 ? 2 * kVItems : kVItems;
   u32x4 kr[kKChunks];
   u32x4 vr[kVRegs];
@@ -232,14 +305,14 @@ struct KvStage {
     const elem* vg = V + ((int64_t)g * seq_len + key0) * kHeadDim;
 #pragma unroll
     for (int i = 0; i < kKChunks; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + NT * i;
       const int row = ch / (kHeadDim / kPer);
       const int col = (ch % (kHeadDim / kPer)) * kPer;
       kr[i] = row < nk ? *reinterpret_cast<const u32x4*>(kg + row * kHeadDim + col) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < kVItems; ++i) {
-      const int it = tid + 256 * i;
+      const int it = tid + NT * i;
       if constexpr (E::is_bf16) {
         const int r = 2 * (it % (kBlock / 2));
         const int col = (it / (kBlock / 2)) * 8;
@@ -259,14 +332,14 @@ struct KvStage {
   __device__ __forceinline__ void store(elem* Ks, elem* Vt, int tid) const {
 #pragma unroll
     for (int i = 0; i < kKChunks; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + NT * i;
       const int row = ch / (kHeadDim / kPer);
       const int col = (ch % (kHeadDim / kPer)) * kPer;
       *reinterpret_cast<u32x4*>(&Ks[row * kKRow + col]) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < kVItems; ++i) {
-      const int it = tid + 256 * i;
+      const int it = tid + NT * i;
       if constexpr (E::is_bf16) {
         const int r = 2 * (it % (kBlock / 2));
         const int col = (it / (kBlock / 2)) * 8;
@@ -382,7 +455,9 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
       // causal mask (keys kk <= lim visible); the scale goes into the exponent's FMA.
       float p[4][16];
       float mx = -INFINITY;
-      const int64_t lim = t - (int64_t)c * kBlock;
+      // 32-bit limit, clamped to [-1, 128], with the lane's key offset 4q folded in
+      const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
+      const int limq = lim - 4 * q;
       const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -391,8 +466,7 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
         for (int r = 0; r < 16; ++r) {
           float x = s[r];
           if (masked) {
-            const int kk = 32 * kt + 8 * (r >> 2) + 4 * q + (r & 3);
-            x = kk <= lim ? x : -INFINITY;
+            x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
           }
           p[kt][r] = x;
           mx = fmaxf(mx, x);
@@ -428,7 +502,7 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            T::store4(dst + 32 * dt + 8 * jj + 4 * q, o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv,
+            T::store4(dst + frag_pos(dt, jj, q), o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv,
                       o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
         if (q == 0) *reinterpret_cast<float2*>(part_ml + prow * 2) = make_float2(mxs, l);
       }
@@ -447,94 +521,483 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
   }
 }
 
-// ---- merge ----------------------------------------------------------------------------------
-// One wave per (token, group). Lane = (head quarter hq = lane / 16, dims 8*(lane % 16) ..+8):
-// every load moves 16 bytes of one head's partial and one instruction covers four heads.
-// Pass 1 finds each head's maximum, pass 2 weights and sums the partials in slot order.
-template <class E, int HMAX>
-__global__ __launch_bounds__(64) void kv_merge_kernel(const typename E::elem* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ block_idx,
-                                                      typename E::elem* __restrict__ out, int G,
-                                                      int Hpg, int top_k, int64_t q_begin) {
+
+// ---- bf16 K staging by direct global->LDS loads (row-swizzled, unpadded) -----------------
+// Row r of the staged block occupies 256 bytes; its 16-byte chunk x sits at position
+// x ^ (r % 16), so a quarter-wave loads one whole row (coalesced) and the S^T operand reads
+// of 8 rows at a time hit distinct banks.
+template <int NT>
+__device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int64_t seq_len,
+                                            uint8_t* kbuf, int tid) {
+  const int64_t key0 = (int64_t)c * kBlock;
+  const int nk = (int)min((int64_t)kBlock, seq_len - key0);
+  const uint16_t* kg = K + ((int64_t)g * seq_len + key0) * kHeadDim;
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int kLoads = kBlock * 256 / 1024;  // 1 KiB loads per block
+#pragma unroll
+  for (int i = 0; i < kLoads / (NT / 64); ++i) {
+    const int li = wave * (kLoads / (NT / 64)) + i;
+    const int r = 4 * li + (lane >> 4);
+    const int chunk = (lane & 15) ^ (r & 15);
+    const int rr = r < nk ? r : nk - 1;  // rows past the sequence end repeat a valid row
+    __builtin_amdgcn_global_load_lds((const void*)(kg + (int64_t)rr * kHeadDim + chunk * 8),
+                                     (__attribute__((address_space(3))) void*)(kbuf + li * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kHeadDim / 16; ++s) {
+    const int pos = (2 * s + q) ^ (m & 15);
+    acc = mfma32(*reinterpret_cast<const u32x4*>(kbuf + m * 256 + pos * 16), qop[s], acc);
+  }
+  return acc;
+}
+
+// O^T += V^T . P^T over one 64-key half of the block (bf16): chunk u of the half holds keys
+// 64 * half + 16 u + {4q .. 4q+3, 8 + 4q .. 8 + 4q + 3}, the keys of its P^T registers.
+__device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const uint16_t* vt,
+                                             int lane, int half) {
+  const int m = lane & 31, q = lane >> 5;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint16_t* vr = vt + (32 * dt + m) * kVRow + 64 * half + 16 * u + 4 * q;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
+    }
+  }
+}
+
+// V^T staging alone (bf16): consecutive lanes take consecutive key pairs of a column chunk.
+template <int NT>
+struct VStage {
+  static constexpr int kItems = (kBlock / 2) * (kHeadDim / 8) / NT;
+  u32x4 vr[2 * kItems];
+  __device__ __forceinline__ void load(const uint16_t* V, int g, int c, int64_t seq_len, int tid) {
+    const int64_t key0 = (int64_t)c * kBlock;
+    const int nk = (int)min((int64_t)kBlock, seq_len - key0);
+    const uint16_t* vg = V + ((int64_t)g * seq_len + key0) * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + NT * i;
+      const int r = 2 * (it % (kBlock / 2));
+      const int col = (it / (kBlock / 2)) * 8;
+      vr[2 * i] = r < nk ? *reinterpret_cast<const u32x4*>(vg + r * kHeadDim + col) : u32x4{0u, 0u, 0u, 0u};
+      vr[2 * i + 1] = r + 1 < nk ? *reinterpret_cast<const u32x4*>(vg + (r + 1) * kHeadDim + col)
+                                 : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int it = tid + NT * i;
+      const int r = 2 * (it % (kBlock / 2));
+      const int col = (it / (kBlock / 2)) * 8;
+      const u32x4 a = vr[2 * i], b = vr[2 * i + 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint32_t*>(&Vt[(col + 2 * j) * kVRow + r]) = (a[j] & 0xffffu) | (b[j] << 16);
+        *reinterpret_cast<uint32_t*>(&Vt[(col + 2 * j + 1) * kVRow + r]) = (a[j] >> 16) | (b[j] & 0xffff0000u);
+      }
+    }
+  }
+};
+
+// ---- query-tile attention over the shared blocks, folding in the rare partials ------------
+// One workgroup (8 waves) per (query tile, group); wave w owns row tile w.
+// For each shared block of the tile (staged once in LDS, the next one loaded while the
+// current is used) every row runs an online softmax step - rows whose token did not keep
+// the block are masked, the local block gets the causal mask. Then each row folds in
+// the partials (o / l, m, l) of its rare entries, computed by the reverse-index path, in
+// slot order, and the final output is written. No partial is stored for shared entries.
+template <class E>
+__global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
+    const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
+    const typename E::elem* __restrict__ V, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ shared, const typename E::elem* __restrict__ part_o,
+    const float* __restrict__ part_ml, typename E::elem* __restrict__ out, int G, int Hpg,
+    int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len) {
   typedef typename E::elem elem;
-  constexpr int HJ = HMAX / 4;  // heads per lane
-  const int lane = threadIdx.x;
-  const int hq = lane >> 4;
-  const int d8 = (lane & 15) * 8;
-  const int64_t rowg = blockIdx.x;  // (i, g)
-  const int64_t i = rowg / G;
-  const int g = (int)(rowg % G);
-  const int64_t t = q_begin + i;
-  const int blocal = (int)(t / kBlock);
-  const int32_t* sel = block_idx + rowg * top_k;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + rowg * top_k * Hpg;
+  typedef TileOps<E> T;
+  constexpr int kBufs = 1;  // fp32 path: one staged block
+  __shared__ __align__(16) elem Ks[kBufs][kBlock * kKRow];
+  __shared__ __align__(16) elem Vt[kBufs][kHeadDim * kVRow];
+  __shared__ int32_t sl[64];
+  __shared__ uint64_t selmask[256];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int epr = 32 / Hpg;
+  const int QT = 8 * epr;
+  const int64_t tile = blockIdx.x / G;
+  const int g = (int)(blockIdx.x % G);
+  const int64_t i0 = tile * QT;
+  const int ntok = (int)min((int64_t)QT, q_count - i0);
   const int Hq = G * Hpg;
-  float M[HJ], L[HJ], acc[HJ][8];
-#pragma unroll
-  for (int j = 0; j < HJ; ++j) {
-    M[j] = -INFINITY;
-    L[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  const int32_t* slist = shared + (tile * G + g) * top_k;
+  if (tid < top_k) sl[tid] = slist[tid];
+  __syncthreads();
+  int ns = 0;
+  while (ns < top_k && sl[ns] >= 0) ++ns;
+  for (int tok = tid; tok < ntok; tok += 512) {
+    const int32_t* tl = block_idx + ((i0 + tok) * G + g) * top_k;
+    const int b = (int)((q_begin + i0 + tok) / kBlock);
+    uint64_t mk = 0;
+    for (int s2 = 0; s2 < top_k; ++s2) {
+      const int c = tl[s2];
+      if (c < 0 || c > b) continue;
+      for (int j = 0; j < ns; ++j)
+        if (sl[j] == c) mk |= 1ull << j;
+    }
+    selmask[tok] = mk;
   }
-  for (int s = 0; s < top_k; ++s) {
-    const int c = sel[s];
-    if (c < 0 || c > blocal) continue;
-#pragma unroll
-    for (int j = 0; j < HJ; ++j)
-      if (hq + 4 * j < Hpg) M[j] = fmaxf(M[j], ml[s * Hpg + hq + 4 * j].x);
+  __syncthreads();
+
+  const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
+  const int n32 = lane & 31, q = lane >> 5;
+  const int e = n32 / Hpg;
+  const int h = n32 - e * Hpg;
+  constexpr int rt = 0;  // one row tile per wave
+  int tok_r[1];
+  bool ok_r[1];
+  int64_t t_r[1];
+  uint64_t mask_r[1];
+  tok_r[0] = wave * epr + e;
+  ok_r[0] = e < epr && tok_r[0] < ntok;
+  t_r[0] = q_begin + i0 + (ok_r[0] ? tok_r[0] : 0);
+  mask_r[0] = ok_r[0] ? selmask[tok_r[0]] : 0ull;
+  float m_r[1] = {-INFINITY}, l_r[1] = {0.f};
+  f32x16 o[1][4] = {};
+
+  KvStage<E, 512> st;
+  if (ns > 0) {
+    st.load(K, V, g, sl[0], seq_len, tid);
+    st.store(Ks[0], Vt[0], tid);
   }
-  for (int s = 0; s < top_k; ++s) {
-    const int c = sel[s];
-    if (c < 0 || c > blocal) continue;
-    const elem* src = part_o + ((rowg * top_k + s) * Hpg) * kHeadDim + d8;
+  __syncthreads();
+  for (int j = 0; j < ns; ++j) {
+    const int c = sl[j];
+    const int buf = kBufs == 2 ? (j & 1) : 0;
+    const bool next = j + 1 < ns;
+    if (kBufs == 2 && next) st.load(K, V, g, sl[j + 1], seq_len, tid);
+    const elem* ks = Ks[buf];
+    const elem* vt = Vt[buf];
+    do {
+      const bool sel = ok_r[rt] && ((mask_r[rt] >> j) & 1ull);
+      if (__ballot(sel) == 0) break;
+      typename T::qop_t qop[T::kQSteps];
+      T::load_q(qop, Q + (t_r[rt] * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, sel);
+      const int lim =
+          (int)min<int64_t>(max<int64_t>(t_r[rt] - (int64_t)c * kBlock, -1), kBlock);
+      const int limq = lim - 4 * q;
+      const bool causal = __ballot(sel && lim < kBlock - 1) != 0;
+      float p[4][16];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < HJ; ++j) {
-      const int h = hq + 4 * j;
-      if (h < Hpg) {
-        const float2 p = ml[s * Hpg + h];
-        const float w = p.y * fast_exp2(p.x - M[j]);
-        L[j] += w;
-        float o[8];
-        if constexpr (E::is_bf16) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(src + h * kHeadDim);
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x16 sv = T::s_tile(&ks[(32 * kt + n32) * kKRow], qop, q);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[2 * e] = bf16_bits_to_f32(v[e] & 0xffffu);
-            o[2 * e + 1] = bf16_bits_to_f32(v[e] >> 16);
+        for (int r = 0; r < 16; ++r) {
+          float x = sel ? sv[r] : -INFINITY;
+          if (causal) {
+            x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
           }
-        } else {
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + h * kHeadDim);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + h * kHeadDim + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = v0[e];
-            o[4 + e] = v1[e];
-          }
+          p[kt][r] = x;
+          mx = fmaxf(mx, x);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] += w * o[e];
       }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_r[rt], mx * qk_scale);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_r[rt] - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ev = m_new == -INFINITY ? 0.f : fast_exp2(fmaf(p[kt][r], qk_scale, -m_new));
+          p[kt][r] = ev;
+          lsum += ev;
+        }
+      lsum += __shfl_xor(lsum, 32, 64);
+      l_r[rt] = l_r[rt] * alpha + lsum;
+      m_r[rt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[rt][dt][r] *= alpha;
+      typename T::pop_t pb[T::kPChunks];
+      T::pack_p(pb, p);
+      T::pv(o[rt], pb, vt, lane);
+    } while (false);
+    if (next) {
+      if constexpr (kBufs == 2) {
+        st.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+      } else {
+        __syncthreads();
+        st.load(K, V, g, sl[j + 1], seq_len, tid);
+        st.store(Ks[0], Vt[0], tid);
+      }
+    }
+    __syncthreads();
+  }
+
+  // Fold in the rare entries' partials (slot order), then normalise and store.
+  {
+    const int64_t irow = i0 + (ok_r[rt] ? tok_r[rt] : 0);
+    const int32_t* tl = block_idx + (irow * G + g) * top_k;
+    const int b = (int)(t_r[rt] / kBlock);
+    for (int s2 = 0; s2 < top_k; ++s2) {
+      const int c = ok_r[rt] ? tl[s2] : -1;
+      bool rare = c >= 0 && c <= b;
+      if (rare)
+        for (int j = 0; j < ns; ++j)
+          if (sl[j] == c) rare = false;
+      if (__ballot(rare) == 0) continue;
+      if (rare) {
+        const int64_t prow = ((irow * G + g) * top_k + s2) * Hpg + h;
+        const float2 ml = *reinterpret_cast<const float2*>(part_ml + prow * 2);
+        const float M = fmaxf(m_r[rt], ml.x);
+        const float a = m_r[rt] == -INFINITY ? 0.f : fast_exp2(m_r[rt] - M);
+        const float wgt = ml.y * fast_exp2(ml.x - M);
+        const elem* src = part_o + prow * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float v4[4];
+            const elem* sp = src + frag_pos(dt, jj, q);
+            if constexpr (E::is_bf16) {
+              const u32x2 w2 = *reinterpret_cast<const u32x2*>(sp);
+              v4[0] = bf16_bits_to_f32(w2[0] & 0xffffu);
+              v4[1] = bf16_bits_to_f32(w2[0] >> 16);
+              v4[2] = bf16_bits_to_f32(w2[1] & 0xffffu);
+              v4[3] = bf16_bits_to_f32(w2[1] >> 16);
+            } else {
+              const f32x4 w4 = *reinterpret_cast<const f32x4*>(sp);
+              v4[0] = w4[0];
+              v4[1] = w4[1];
+              v4[2] = w4[2];
+              v4[3] = w4[3];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[rt][dt][4 * jj + r] = o[rt][dt][4 * jj + r] * a + wgt * v4[r];
+          }
+        l_r[rt] = l_r[rt] * a + wgt;
+        m_r[rt] = M;
+      }
+    }
+    if (ok_r[rt]) {
+      const float inv = l_r[rt] > 0.f ? 1.f / l_r[rt] : 0.f;
+      elem* dst = out + (t_r[rt] * Hq + (int64_t)g * Hpg + h) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          T::store4(dst + 32 * dt + 8 * jj + 4 * q, o[rt][dt][4 * jj] * inv,
+                    o[rt][dt][4 * jj + 1] * inv, o[rt][dt][4 * jj + 2] * inv,
+                    o[rt][dt][4 * jj + 3] * inv);
     }
   }
-  elem* dst = out + (t * Hq + (int64_t)g * Hpg) * kHeadDim + d8;
+}
+
+// ---- query-tile attention over the shared blocks, folding in the rare partials ------------
+// One workgroup (8 waves) per (query tile, group); wave w owns row tile w.
+// For each shared block of the tile (staged once in LDS, the next one loaded while the
+// current is used) every row runs an online softmax step - rows whose token did not keep
+// the block are masked, the local block gets the causal mask. Then each row folds in
+// the partials (o / l, m, l) of its rare entries, computed by the reverse-index path, in
+// slot order, and the final output is written. No partial is stored for shared entries.
+// bf16 form: 4 waves with one row tile each (a query tile is 4 row tiles) and about 66 KB
+// of LDS, so two workgroups share a CU: while one stages a block or reads partials, the
+// other keeps the matrix cores busy. Q stays in registers across the shared blocks. A
+// row's running maximum is raised only when a new score exceeds it by more than 8 (log2
+// units), so the accumulator is rescaled rarely and every exponential stays below 2^8;
+// the final division by the row sum makes the result the same up to rounding.
+template <int KMAX>
+__global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ shared, const uint16_t* __restrict__ part_o,
+    const float* __restrict__ part_ml, uint16_t* __restrict__ out, int G, int Hpg, int top_k,
+    int64_t q_begin, int64_t q_count, int64_t seq_len) {
+  typedef TileOps<BF16> T;
+  __shared__ __align__(16) uint8_t Kb[kBlock * 256];
+  __shared__ __align__(16) uint16_t Vt[kHeadDim * kVRow];
+  __shared__ int32_t sl[64];
+  __shared__ uint64_t selmask[128];   // per token: which shared blocks it keeps
+  __shared__ uint64_t raremask[128];  // per token: which slots go through the partials
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int epr = 32 / Hpg;
+  const int QT = 4 * epr;
+  const int64_t tile = blockIdx.x / G;
+  const int g = (int)(blockIdx.x % G);
+  const int64_t i0 = tile * QT;
+  const int ntok = (int)min((int64_t)QT, q_count - i0);
+  const int Hq = G * Hpg;
+  if (tid < top_k) sl[tid] = shared[(tile * G + g) * top_k + tid];
+  __syncthreads();
+  int ns = 0;
+  while (ns < top_k && sl[ns] >= 0) ++ns;
+  if (tid < ntok) {
+    const int32_t* tl = block_idx + ((i0 + tid) * G + g) * top_k;
+    const int b = (int)((q_begin + i0 + tid) / kBlock);
+    int cs[KMAX];
 #pragma unroll
-  for (int j = 0; j < HJ; ++j) {
-    const int h = hq + 4 * j;
-    if (h < Hpg) {
-      const float inv = L[j] > 0.f ? 1.f / L[j] : 0.f;
-      if constexpr (E::is_bf16) {
-        *reinterpret_cast<u32x4*>(dst + h * kHeadDim) =
-            u32x4{pack_bf16x2(acc[j][0] * inv, acc[j][1] * inv), pack_bf16x2(acc[j][2] * inv, acc[j][3] * inv),
-                  pack_bf16x2(acc[j][4] * inv, acc[j][5] * inv), pack_bf16x2(acc[j][6] * inv, acc[j][7] * inv)};
-      } else {
-        *reinterpret_cast<f32x4*>(dst + h * kHeadDim) =
-            f32x4{acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv};
-        *reinterpret_cast<f32x4*>(dst + h * kHeadDim + 4) =
-            f32x4{acc[j][4] * inv, acc[j][5] * inv, acc[j][6] * inv, acc[j][7] * inv};
-      }
+    for (int s2 = 0; s2 < KMAX; ++s2) cs[s2] = s2 < top_k ? tl[s2] : -1;  // all loads in flight
+    uint64_t mk = 0, rk = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      const int c = cs[s2];
+      if (c < 0 || c > b) continue;
+      bool found = false;
+      for (int j = 0; j < ns; ++j)
+        if (sl[j] == c) {
+          mk |= 1ull << j;
+          found = true;
+        }
+      if (!found) rk |= 1ull << s2;
     }
+    selmask[tid] = mk;
+    raremask[tid] = rk;
+  }
+
+  const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
+  const int n32 = lane & 31, q = lane >> 5;
+  const int e = n32 / Hpg;
+  const int h = n32 - e * Hpg;
+  const int tok = wave * epr + e;
+  const bool ok = e < epr && tok < ntok;
+  const int64_t irow = i0 + (ok ? tok : 0);
+  const int64_t t = q_begin + irow;
+  T::qop_t qop[T::kQSteps];
+  T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+  __syncthreads();
+  const uint64_t mymask = ok ? selmask[tok] : 0ull;
+  const uint64_t myrare = ok ? raremask[tok] : 0ull;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[4] = {};
+  VStage<256> vst;
+
+  for (int j = 0; j < ns; ++j) {
+    const int c = sl[j];
+    if (j > 0) __syncthreads();  // every wave is done with the previous block
+    k_block_dma<256>(K, g, c, seq_len, Kb, tid);
+    vst.load(V, g, c, seq_len, tid);
+    MSA_WAIT_VMCNT(0);
+    vst.store(Vt, tid);
+    __syncthreads();
+    const bool sel = (mymask >> j) & 1ull;
+    if (__ballot(sel) == 0) continue;
+    const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
+    const int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
+    const bool causal = __ballot(sel && lim < kBlock - 1) != 0;
+    // the block's 128 keys in two halves of 64, one online-softmax step each
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float p[2][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const int kt = 2 * half + kk2;
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sel ? sv[r] : -INFINITY;
+          if (causal) {
+            x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
+          }
+          p[kk2][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mxs = mx * qk_scale;
+      const bool raise = mxs > m_run + 8.f;  // false while the row has no score (-inf)
+      if (__ballot(raise)) {
+        const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
+        m_run = raise ? mxs : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;  // masked scores give exp2(-inf) = 0
+      float lsum = 0.f;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ev = fast_exp2(fmaf(p[kk2][r], qk_scale, mneg));
+          p[kk2][r] = ev;
+          lsum += ev;
+        }
+      lsum += __shfl_xor(lsum, 32, 64);
+      l_run += lsum;
+      u32x4 pb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* pr = &p[u >> 1][8 * (u & 1)];
+        pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+      }
+      pv_half_bf16(o, pb, Vt, lane, half);
+    }
+  }
+
+  // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
+  // adds the weighted partials, whose 64 values per lane are contiguous (fragment order).
+  if (__ballot(myrare != 0)) {
+    const int64_t prow0 = (irow * G + g) * top_k * Hpg + h;
+    const float2* ml2 = reinterpret_cast<const float2*>(part_ml);
+    float M = m_run;
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2)
+      if ((myrare >> s2) & 1ull) M = fmaxf(M, ml2[prow0 + (int64_t)s2 * Hpg].x);
+    const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+    l_run *= a;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= a;
+#pragma unroll 2
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      const bool rare = (myrare >> s2) & 1ull;
+      if (!__ballot(rare)) continue;
+      const int64_t prow = prow0 + (int64_t)s2 * Hpg;
+      const float2 ml = rare ? ml2[prow] : make_float2(-INFINITY, 0.f);
+      const u32x4* src = reinterpret_cast<const u32x4*>(part_o + prow * kHeadDim + 64 * q);
+      u32x4 w4[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w4[i] = rare ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      const float w = rare ? ml.y * fast_exp2(ml.x - M) : 0.f;
+      l_run += w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) {
+          const uint32_t bits = k2 & 1 ? w4[i][k2 >> 1] >> 16 : w4[i][k2 >> 1] & 0xffffu;
+          const int r = 4 * (2 * (i & 1) + (k2 >> 2)) + (k2 & 3);
+          o[i >> 1][r] = fmaf(w, bf16_bits_to_f32(bits), o[i >> 1][r]);
+        }
+    }
+  }
+  if (ok) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* dst = out + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        T::store4(dst + 32 * dt + 8 * jj + 4 * q, o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv,
+                  o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
   }
 }
 
@@ -545,7 +1008,9 @@ size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, 
   const int64_t nb = (int64_t)G * nblk;
   const int64_t E = q_count * G * top_k;
   const size_t es = bf16 ? 2 : 4;
-  return al256((size_t)nb * kStripes * 4) * 2 + al256((size_t)(nb + 1) * 4) +
+  const int64_t ntiles = (q_count + qtile_tokens(Hpg, bf16) - 1) / qtile_tokens(Hpg, bf16);
+  return al256((size_t)ntiles * G * top_k * 4) +
+         al256((size_t)nb * kStripes * 4) * 2 + al256((size_t)(nb + 1) * 4) +
          al256((size_t)E * 4) + al256((size_t)E * Hpg * 2 * 4) +
          al256((size_t)E * Hpg * kHeadDim * es);
 }
@@ -558,7 +1023,11 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
   typedef typename E::elem elem;
   const int64_t nb = (int64_t)G * nblk;
   const int64_t n_entries = q_count * G * top_k;
+  const int QT = qtile_tokens(Hpg, E::is_bf16 ? 1 : 0);
+  const int64_t ntiles = (q_count + QT - 1) / QT;
   char* w = static_cast<char*>(ws);
+  int32_t* shared = reinterpret_cast<int32_t*>(w);
+  w += al256((size_t)ntiles * G * top_k * 4);
   int32_t* count = reinterpret_cast<int32_t*>(w);
   w += al256((size_t)nb * kStripes * 4);
   int32_t* cursor = reinterpret_cast<int32_t*>(w);
@@ -575,25 +1044,35 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
   const int64_t ncnt = nb * kStripes;
   hipLaunchKernelGGL(kv_zero_kernel, dim3((unsigned)std::min<int64_t>((ncnt + 255) / 256, 4096)),
                      dim3(256), 0, st, count, ncnt);
+  const int64_t npairs = ntiles * G;
+  hipLaunchKernelGGL(kv_classify_kernel, dim3((unsigned)((npairs + 3) / 4)), dim3(256), 0, st,
+                     block_idx, shared, G, top_k, q_begin, q_count, QT, npairs);
   hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, count);
+                     top_k, q_begin, nblk, shared, QT, count);
   hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, st, count, nb, cursor, offset);
   hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, cursor, sorted);
+                     top_k, q_begin, nblk, shared, QT, cursor, sorted);
   const unsigned tiles = (unsigned)((n_entries + kTile - 1) / kTile);
   hipLaunchKernelGGL((kv_attn_kernel<E>), dim3(tiles), dim3(256), 0, st, (const elem*)q,
                      (const elem*)k, (const elem*)v, block_idx, sorted, offset + nb, part_o,
                      part_ml, G, Hpg, top_k, q_begin, seq_len);
-  const dim3 mgrid((unsigned)(q_count * G));
-  if (Hpg <= 4)
-    hipLaunchKernelGGL((kv_merge_kernel<E, 4>), mgrid, dim3(64), 0, st, part_o, part_ml,
-                       block_idx, (elem*)out, G, Hpg, top_k, q_begin);
-  else if (Hpg <= 8)
-    hipLaunchKernelGGL((kv_merge_kernel<E, 8>), mgrid, dim3(64), 0, st, part_o, part_ml,
-                       block_idx, (elem*)out, G, Hpg, top_k, q_begin);
-  else
-    hipLaunchKernelGGL((kv_merge_kernel<E, 16>), mgrid, dim3(64), 0, st, part_o, part_ml,
-                       block_idx, (elem*)out, G, Hpg, top_k, q_begin);
+  if constexpr (E::is_bf16) {
+    if (top_k <= 16)
+      hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(256), 0, st,
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
+                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
+                         q_begin, q_count, seq_len);
+    else
+      hipLaunchKernelGGL((qtile_attn_bf16_kernel<64>), dim3((unsigned)npairs), dim3(256), 0, st,
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
+                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
+                         q_begin, q_count, seq_len);
+  }
+  if constexpr (!E::is_bf16)
+    hipLaunchKernelGGL((qtile_attn_kernel<E>), dim3((unsigned)npairs), dim3(512), 0, st,
+                       (const elem*)q, (const elem*)k, (const elem*)v, block_idx, shared,
+                       (const elem*)part_o, part_ml, (elem*)out, G, Hpg, top_k, q_begin, q_count,
+                       seq_len);
   return hipGetLastError();
 }
 

@@ -19,9 +19,6 @@
 
 namespace msa {
 
-// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding).
-#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
-
 template <class E>
 struct Operand;
 template <>

@@ -6,6 +6,10 @@
 
 namespace msa {
 
+// s_waitcnt vmcnt(n) with the other counters at their maximum (gfx9 encoding): waits until
+// at most n of this wave's vector-memory operations are outstanding.
+#define MSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
