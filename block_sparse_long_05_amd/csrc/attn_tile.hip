@@ -540,7 +540,8 @@ __device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int
     const int r = 4 * li + (lane >> 4);
     const int chunk = (lane & 15) ^ (r & 15);
     const int rr = r < nk ? r : nk - 1;  // rows past the sequence end repeat a valid row
-    __builtin_amdgcn_global_load_lds((const void*)(kg + (int64_t)rr * kHeadDim + chunk * 8),
+    const uint32_t off = (uint32_t)(rr * kHeadDim + chunk * 8);  // 32-bit: uniform base + offset
+    __builtin_amdgcn_global_load_lds((const void*)(kg + off),
                                      (__attribute__((address_space(3))) void*)(kbuf + li * 1024),
                                      16, 0, 0);
   }
@@ -569,6 +570,213 @@ __device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const u
       const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
       o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
+    }
+  }
+}
+
+// O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the
+// row-swizzled layout of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
+// lane i of a 16-lane group column i % 4 of the 8-byte rows that lanes 4 j + i / 4
+// (j = 0..3) address. Lane (m = lane % 32, q = lane / 32) needs D column 32 dt + m of
+// keys 16 u + 4 q + 0..3 (then + 8): so lane r of its group addresses key row
+// 16 u + 4 q + r / 4, columns 32 dt + 16 ((lane / 16) % 2) + 4 (r % 4) .. + 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void pv_half_tr(f32x16* o, const u32x4* pb, const uint8_t* vbuf,
+                                           int lane, int half) {
+  // Chunk (4 dt + c0) of key row rr sits at position (4 dt + c0) ^ rr = 4 (dt ^ q) + cx, with
+  // c0 = 2 hx + (r % 4) / 2, cx = c0 ^ (rr % 4) and q = rr / 4; row rr + 8 gives
+  // 4 (dt ^ q ^ 2) + cx. Since dt ^ q = dt + q for even dt and dt - q for odd dt, two
+  // lane bases and immediate offsets cover all reads.
+  const int q = lane >> 5, hx = (lane >> 4) & 1, r = lane & 15;
+  const int rr = 4 * q + (r >> 2);
+  const int cx = (2 * hx + ((r & 3) >> 1)) ^ (rr & 3);
+  const uint8_t* base = vbuf + rr * 256 + (r & 1) * 8 + 16 * cx;
+  const uint8_t* b_even = base + 64 * q;
+  const uint8_t* b_odd = base - 64 * q;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row0 = 64 * half + 16 * u;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint8_t* bb = (dt & 1) ? b_odd : b_even;
+      const u32x2 lo = lds_read_tr16(bb + row0 * 256 + 64 * dt);
+      const u32x2 hi = lds_read_tr16(bb + (row0 + 8) * 256 + 64 * (dt ^ 2));
+      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
+    }
+  }
+}
+
+// ---- reverse-index tile attention, bf16 ----------------------------------------------------
+// K and V of each run's block are staged row-major by direct global->LDS loads into one
+// 64 KB buffer, so two workgroups share a CU and one's staging and query gathers overlap
+// the other's MFMA work. Each row tile covers the block in two 64-key halves with the
+// lazily raised maximum of the query-tile kernel; the partial is written in fragment
+// order (16-byte stores) with the row's reference maximum and sum.
+__global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ offset_total,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml, int G, int Hpg, int top_k,
+    int64_t q_begin, int64_t seq_len) {
+  typedef TileOps<BF16> T;
+  __shared__ __align__(16) uint8_t Kb[kBlock * 256];
+  __shared__ __align__(16) uint8_t Vb[kBlock * 256];
+  __shared__ int32_t ids[kTile];
+  __shared__ int32_t keys[kTile];
+  __shared__ int32_t run_start[kTile + 1];
+  __shared__ uint64_t bmask[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t total = *offset_total;
+  const int64_t e0 = (int64_t)blockIdx.x * kTile;
+  if (e0 >= total) return;
+  const int n = (int)min((int64_t)kTile, total - e0);
+  const int Hq = G * Hpg;
+  const int epr = 32 / Hpg;  // entries per 32-row tile
+  int32_t mykey = -1;
+  if (tid < n) {
+    const int32_t id = sorted[e0 + tid];
+    ids[tid] = id;
+    mykey = (int32_t)(((id / top_k) % G) << 24) | block_idx[id];  // (g, c): g < 64, c < 2^24
+    keys[tid] = mykey;
+  }
+  __syncthreads();
+  // Runs of equal (g, c): boundary flags -> ballots -> run_start[] by prefix popcount.
+  const bool boundary = tid < n && (tid == 0 || keys[tid - 1] != mykey);
+  const uint64_t wm = __ballot(boundary);
+  if (lane == 0) bmask[wave] = wm;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += __popcll(bmask[w]);
+  const int nruns = __popcll(bmask[0]) + __popcll(bmask[1]) + __popcll(bmask[2]) + __popcll(bmask[3]);
+  if (boundary) run_start[before + __popcll(wm & ((1ull << lane) - 1ull))] = tid;
+  if (tid == 0) run_start[nruns] = n;
+  __syncthreads();
+
+  const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
+  const int n32 = lane & 31, q = lane >> 5;
+  const int e = n32 / Hpg;
+  const int h = n32 - e * Hpg;
+
+  for (int j = 0; j < nruns; ++j) {
+    // wave-uniform values in scalar registers (the staging addresses then use them)
+    const int r0 = __builtin_amdgcn_readfirstlane(run_start[j]);
+    const int r1 = __builtin_amdgcn_readfirstlane(run_start[j + 1]);
+    const int key = __builtin_amdgcn_readfirstlane(keys[r0]);
+    const int g = key >> 24;
+    const int c = key & 0xffffff;
+    if (j > 0) __syncthreads();  // every wave is done with the previous block
+    // Lane-derived addresses are recomputed in each loop instead of being kept live
+    // across it (the empty asm hides that the lane id does not change).
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
+    k_block_dma<256>(V, g, c, seq_len, Vb, tid_v);
+    const int nrt = (r1 - r0 + epr - 1) / epr;
+    auto row_of = [&](int rt, int32_t& id, int64_t& t) {
+      const int ent = r0 + rt * epr + e;
+      const bool ok = e < epr && ent < r1;
+      id = ok ? ids[ent] : 0;
+      t = q_begin + (id / top_k) / G;
+      return ok;
+    };
+    T::qop_t qop[T::kQSteps];
+    int32_t id = 0;
+    int64_t t = 0;
+    bool ok = false;
+    if (wave < nrt) {
+      ok = row_of(wave, id, t);
+      T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+    }
+    MSA_WAIT_VMCNT(0);  // this wave's K and V loads have landed
+    __syncthreads();
+    for (int rt = wave; rt < nrt; rt += 4) {
+      int lane_v = lane;
+      asm volatile("" : "+v"(lane_v));
+      const int n32v = lane_v & 31, qv = lane_v >> 5;
+      const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
+      const int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
+      const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
+      const int32_t cur_id = id;
+      const bool cur_ok = ok;
+      float m_run = -INFINITY, l_run = 0.f;
+      f32x16 o[4] = {};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[2][16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const int kt = 2 * half + kk2;
+          const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float x = sv[r];
+            if (masked) x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
+            p[kk2][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        if (half == 1 && rt + 4 < nrt) {  // S^T is done with this row tile's queries
+          ok = row_of(rt + 4, id, t);
+          T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mxs = mx * qk_scale;
+        const bool raise = mxs > m_run + 8.f;  // the first half always sets it (key 128c <= t)
+        if (__ballot(raise)) {
+          const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
+          m_run = raise ? mxs : m_run;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        float lsum = 0.f;
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float ev = fast_exp2(fmaf(p[kk2][r], qk_scale, -m_run));
+            p[kk2][r] = ev;
+            lsum += ev;
+          }
+        lsum += __shfl_xor(lsum, 32, 64);
+        l_run += lsum;
+        u32x4 pb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float* pr = &p[u >> 1][8 * (u & 1)];
+          pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+        }
+        pv_half_tr(o, pb, Vb, lane_v, half);
+      }
+      if (cur_ok) {
+        const float inv = 1.f / l_run;
+        const int64_t prow = (int64_t)cur_id * Hpg + h;
+        uint16_t* dst = part_o + prow * kHeadDim + 64 * q;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int hp = 0; hp < 2; ++hp) {
+            const int b0 = 8 * hp;
+            *reinterpret_cast<u32x4*>(dst + 16 * dt + 8 * hp) =
+                u32x4{pack_bf16x2(o[dt][b0] * inv, o[dt][b0 + 1] * inv),
+                      pack_bf16x2(o[dt][b0 + 2] * inv, o[dt][b0 + 3] * inv),
+                      pack_bf16x2(o[dt][b0 + 4] * inv, o[dt][b0 + 5] * inv),
+                      pack_bf16x2(o[dt][b0 + 6] * inv, o[dt][b0 + 7] * inv)};
+          }
+        if (q == 0) *reinterpret_cast<float2*>(part_ml + prow * 2) = make_float2(m_run, l_run);
+      }
     }
   }
 }
@@ -814,7 +1022,8 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
 // slot order, and the final output is written. No partial is stored for shared entries.
 // bf16 form: 4 waves with one row tile each (a query tile is 4 row tiles) and about 66 KB
 // of LDS, so two workgroups share a CU: while one stages a block or reads partials, the
-// other keeps the matrix cores busy. Q stays in registers across the shared blocks. A
+// other keeps the matrix cores busy. K and V are both staged row-major by direct
+// global->LDS loads; PV reads V through the LDS transpose read. Q stays in registers across the shared blocks. A
 // row's running maximum is raised only when a new score exceeds it by more than 8 (log2
 // units), so the accumulator is rescaled rarely and every exponential stays below 2^8;
 // the final division by the row sum makes the result the same up to rounding.
@@ -827,7 +1036,7 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
     int64_t q_begin, int64_t q_count, int64_t seq_len) {
   typedef TileOps<BF16> T;
   __shared__ __align__(16) uint8_t Kb[kBlock * 256];
-  __shared__ __align__(16) uint16_t Vt[kHeadDim * kVRow];
+  __shared__ __align__(16) uint8_t Vb[kBlock * 256];
   __shared__ int32_t sl[64];
   __shared__ uint64_t selmask[128];   // per token: which shared blocks it keeps
   __shared__ uint64_t raremask[128];  // per token: which slots go through the partials
@@ -883,15 +1092,13 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
   const uint64_t myrare = ok ? raremask[tok] : 0ull;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4] = {};
-  VStage<256> vst;
 
   for (int j = 0; j < ns; ++j) {
-    const int c = sl[j];
+    const int c = __builtin_amdgcn_readfirstlane(sl[j]);  // uniform: scalar staging base
     if (j > 0) __syncthreads();  // every wave is done with the previous block
     k_block_dma<256>(K, g, c, seq_len, Kb, tid);
-    vst.load(V, g, c, seq_len, tid);
+    k_block_dma<256>(V, g, c, seq_len, Vb, tid);
     MSA_WAIT_VMCNT(0);
-    vst.store(Vt, tid);
     __syncthreads();
     const bool sel = (mymask >> j) & 1ull;
     if (__ballot(sel) == 0) continue;
@@ -948,7 +1155,7 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
         pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
       }
-      pv_half_bf16(o, pb, Vt, lane, half);
+      pv_half_tr(o, pb, Vb, lane, half);
     }
   }
 
@@ -1053,9 +1260,14 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
   hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
                      top_k, q_begin, nblk, shared, QT, cursor, sorted);
   const unsigned tiles = (unsigned)((n_entries + kTile - 1) / kTile);
-  hipLaunchKernelGGL((kv_attn_kernel<E>), dim3(tiles), dim3(256), 0, st, (const elem*)q,
-                     (const elem*)k, (const elem*)v, block_idx, sorted, offset + nb, part_o,
-                     part_ml, G, Hpg, top_k, q_begin, seq_len);
+  if constexpr (E::is_bf16)
+    hipLaunchKernelGGL(kv_attn_bf16_kernel, dim3(tiles), dim3(256), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, block_idx, sorted, offset + nb,
+                       (uint16_t*)part_o, part_ml, G, Hpg, top_k, q_begin, seq_len);
+  else
+    hipLaunchKernelGGL((kv_attn_kernel<E>), dim3(tiles), dim3(256), 0, st, (const elem*)q,
+                       (const elem*)k, (const elem*)v, block_idx, sorted, offset + nb, part_o,
+                       part_ml, G, Hpg, top_k, q_begin, seq_len);
   if constexpr (E::is_bf16) {
     if (top_k <= 16)
       hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(256), 0, st,
