@@ -20,6 +20,10 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # Packed fp32 VALU ops stay off: the compiler must not form v_pk_* fp32 math.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Inputs are finite (NaN/Inf inputs are undefined behaviour of the ABI), so the
+    # compiler need not quiet MFMA results before every max (IEEE-mode canonicalising
+    # v_max_f32 x, x would otherwise double the max-pooling VALU work).
+    "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

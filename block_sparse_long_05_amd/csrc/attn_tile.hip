@@ -526,7 +526,12 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
 // Row r of the staged block occupies 256 bytes; its 16-byte chunk x sits at position
 // x ^ (r % 16), so a quarter-wave loads one whole row (coalesced) and the S^T operand reads
 // of 8 rows at a time hit distinct banks.
-template <int NT>
+// V blocks use another row swizzle (kVSwz): chunk x of row r sits at position
+// x ^ (4 (r % 4) + (r / 4) % 4), which keeps the transpose reads of PV (4 rows x 4
+// chunks per half-wave) on 16 distinct positions.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int NT, bool kVSwz = false>
 __device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int64_t seq_len,
                                             uint8_t* kbuf, int tid) {
   const int64_t key0 = (int64_t)c * kBlock;
@@ -538,7 +543,7 @@ __device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int
   for (int i = 0; i < kLoads / (NT / 64); ++i) {
     const int li = wave * (kLoads / (NT / 64)) + i;
     const int r = 4 * li + (lane >> 4);
-    const int chunk = (lane & 15) ^ (r & 15);
+    const int chunk = (lane & 15) ^ (kVSwz ? v_swz(r) : (r & 15));
     const int rr = r < nk ? r : nk - 1;  // rows past the sequence end repeat a valid row
     const uint32_t off = (uint32_t)(rr * kHeadDim + chunk * 8);  // 32-bit: uniform base + offset
     __builtin_amdgcn_global_load_lds((const void*)(kg + off),
@@ -574,8 +579,8 @@ __device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const u
   }
 }
 
-// O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the
-// row-swizzled layout of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
+// O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the V
+// row swizzle of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
 // lane i of a 16-lane group column i % 4 of the 8-byte rows that lanes 4 j + i / 4
 // (j = 0..3) address. Lane (m = lane % 32, q = lane / 32) needs D column 32 dt + m of
 // keys 16 u + 4 q + 0..3 (then + 8): so lane r of its group addresses key row
@@ -589,24 +594,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
 
 __device__ __forceinline__ void pv_half_tr(f32x16* o, const u32x4* pb, const uint8_t* vbuf,
                                            int lane, int half) {
-  // Chunk (4 dt + c0) of key row rr sits at position (4 dt + c0) ^ rr = 4 (dt ^ q) + cx, with
-  // c0 = 2 hx + (r % 4) / 2, cx = c0 ^ (rr % 4) and q = rr / 4; row rr + 8 gives
-  // 4 (dt ^ q ^ 2) + cx. Since dt ^ q = dt + q for even dt and dt - q for odd dt, two
-  // lane bases and immediate offsets cover all reads.
+  // Key row 16 u' + 4 q + j (+ 8 for the second read) holds chunk (4 dt + c0) at position
+  // 4 (dt ^ j) + (c0 ^ q) (+ 2, xor, for the second read), with c0 = 2 hx + (r % 4) / 2.
   const int q = lane >> 5, hx = (lane >> 4) & 1, r = lane & 15;
-  const int rr = 4 * q + (r >> 2);
-  const int cx = (2 * hx + ((r & 3) >> 1)) ^ (rr & 3);
-  const uint8_t* base = vbuf + rr * 256 + (r & 1) * 8 + 16 * cx;
-  const uint8_t* b_even = base + 64 * q;
-  const uint8_t* b_odd = base - 64 * q;
+  const int j = r >> 2;
+  const int c0 = 2 * hx + ((r & 3) >> 1);
+  const uint8_t* base = vbuf + (4 * q + j) * 256 + (r & 1) * 8;
+  const uint8_t* lo_b[4];
+  const uint8_t* hi_b[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    lo_b[dt] = base + 64 * (dt ^ j) + 16 * (c0 ^ q);
+    hi_b[dt] = base + 8 * 256 + 64 * (dt ^ j) + 16 * (c0 ^ q ^ 2);
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row0 = 64 * half + 16 * u;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const uint8_t* bb = (dt & 1) ? b_odd : b_even;
-      const u32x2 lo = lds_read_tr16(bb + row0 * 256 + 64 * dt);
-      const u32x2 hi = lds_read_tr16(bb + (row0 + 8) * 256 + 64 * (dt ^ 2));
+      const u32x2 lo = lds_read_tr16(lo_b[dt] + row0 * 256);
+      const u32x2 hi = lds_read_tr16(hi_b[dt] + row0 * 256);
       o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
     }
   }
@@ -678,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
     int tid_v = tid;
     asm volatile("" : "+v"(tid_v));
     k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
-    k_block_dma<256>(V, g, c, seq_len, Vb, tid_v);
+    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
     const int nrt = (r1 - r0 + epr - 1) / epr;
     auto row_of = [&](int rt, int32_t& id, int64_t& t) {
       const int ent = r0 + rt * epr + e;
@@ -1096,8 +1103,14 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
   for (int j = 0; j < ns; ++j) {
     const int c = __builtin_amdgcn_readfirstlane(sl[j]);  // uniform: scalar staging base
     if (j > 0) __syncthreads();  // every wave is done with the previous block
-    k_block_dma<256>(K, g, c, seq_len, Kb, tid);
-    k_block_dma<256>(V, g, c, seq_len, Vb, tid);
+    // lane-derived addresses are recomputed per block rather than kept live (the empty
+    // asm hides that the thread id does not change)
+    int tid_v = tid;
+    asm volatile("" : "+v"(tid_v));
+    const int lane_v = tid_v & 63;
+    const int n32v = lane_v & 31, qv = lane_v >> 5;
+    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
+    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
     MSA_WAIT_VMCNT(0);
     __syncthreads();
     const bool sel = (mymask >> j) & 1ull;
@@ -1113,7 +1126,7 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const int kt = 2 * half + kk2;
-        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = sel ? sv[r] : -INFINITY;
@@ -1155,7 +1168,7 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
         pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
       }
-      pv_half_tr(o, pb, Vb, lane, half);
+      pv_half_tr(o, pb, Vb, lane_v, half);
     }
   }
 
