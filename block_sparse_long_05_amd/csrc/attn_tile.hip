@@ -623,8 +623,11 @@ __device__ __forceinline__ void pv_half_tr(f32x16* o, const u32x4* pb, const uin
 // K and V of each run's block are staged row-major by direct global->LDS loads into one
 // 64 KB buffer, so two workgroups share a CU and one's staging and query gathers overlap
 // the other's MFMA work. Each row tile covers the block in two 64-key halves with the
-// lazily raised maximum of the query-tile kernel; the partial is written in fragment
-// order (16-byte stores) with the row's reference maximum and sum.
+// lazily raised maximum of the query-tile kernel. An entry's partial (Hpg heads x 128
+// values, bf16) is one lane-interleaved block: the 16-byte chunk i (values
+// 32 (i / 2) + 8 (i % 2) .. of the lane's fragment) of head h, lane group q sits at
+// element i * 16 Hpg + 8 (h + Hpg q), so each store instruction writes whole cache lines.
+// (m, l) = the row's reference maximum and sum go to part_ml.
 __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
@@ -770,13 +773,14 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       if (cur_ok) {
         const float inv = 1.f / l_run;
         const int64_t prow = (int64_t)cur_id * Hpg + h;
-        uint16_t* dst = part_o + prow * kHeadDim + 64 * q;
+        // lane-interleaved entry block: chunk i of lane (h, q) at i * 16 Hpg + 8 (h + Hpg q)
+        uint16_t* dst = part_o + (int64_t)cur_id * Hpg * kHeadDim + 8 * (h + Hpg * q);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int hp = 0; hp < 2; ++hp) {
             const int b0 = 8 * hp;
-            *reinterpret_cast<u32x4*>(dst + 16 * dt + 8 * hp) =
+            *reinterpret_cast<u32x4*>(dst + (2 * dt + hp) * 16 * Hpg) =
                 u32x4{pack_bf16x2(o[dt][b0] * inv, o[dt][b0 + 1] * inv),
                       pack_bf16x2(o[dt][b0 + 2] * inv, o[dt][b0 + 3] * inv),
                       pack_bf16x2(o[dt][b0 + 4] * inv, o[dt][b0 + 5] * inv),
@@ -1173,7 +1177,8 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
   }
 
   // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
-  // adds the weighted partials, whose 64 values per lane are contiguous (fragment order).
+  // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
+  // them: each load instruction covers whole cache lines).
   if (__ballot(myrare != 0)) {
     const int64_t prow0 = (irow * G + g) * top_k * Hpg + h;
     const float2* ml2 = reinterpret_cast<const float2*>(part_ml);
@@ -1193,10 +1198,11 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
       if (!__ballot(rare)) continue;
       const int64_t prow = prow0 + (int64_t)s2 * Hpg;
       const float2 ml = rare ? ml2[prow] : make_float2(-INFINITY, 0.f);
-      const u32x4* src = reinterpret_cast<const u32x4*>(part_o + prow * kHeadDim + 64 * q);
+      const uint16_t* src = part_o + (prow - h) * kHeadDim + 8 * (h + Hpg * q);
       u32x4 w4[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w4[i] = rare ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 8; ++i)
+        w4[i] = rare ? *reinterpret_cast<const u32x4*>(src + i * 16 * Hpg) : u32x4{0u, 0u, 0u, 0u};
       const float w = rare ? ml.y * fast_exp2(ml.x - M) : 0.f;
       l_run += w;
 #pragma unroll
