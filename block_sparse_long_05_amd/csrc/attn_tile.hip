@@ -1227,6 +1227,127 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
   }
 }
 
+// ---- dense causal GQA prefill, bf16 (the dense baseline the sparse path is compared with) --
+// Flash-style: one workgroup per (query tile of 4 row tiles, group); every visible block is
+// streamed through LDS (K and V by direct global->LDS loads, PV through transpose reads),
+// each row keeps an online softmax with the lazily raised maximum of the query-tile
+// kernel, and the output is written once at the end. The latest (heaviest) tiles start
+// first; two workgroups share a CU.
+__global__ __launch_bounds__(256, 2) void dense_attn_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ out, int G, int Hpg,
+    int64_t q_begin, int64_t q_count, int64_t seq_len) {
+  typedef TileOps<BF16> T;
+  __shared__ __align__(16) uint8_t Kb[kBlock * 256];
+  __shared__ __align__(16) uint8_t Vb[kBlock * 256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int epr = 32 / Hpg;
+  const int QT = 4 * epr;
+  const int64_t ntiles = (q_count + QT - 1) / QT;
+  const int64_t tile = ntiles - 1 - (int64_t)(blockIdx.x / G);
+  const int g = (int)(blockIdx.x % G);
+  const int64_t i0 = tile * QT;
+  const int ntok = (int)min((int64_t)QT, q_count - i0);
+  const int Hq = G * Hpg;
+  const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
+  const int n32 = lane & 31, q = lane >> 5;
+  const int e = n32 / Hpg;
+  const int h = n32 - e * Hpg;
+  const int tok = wave * epr + e;
+  const bool ok = e < epr && tok < ntok;
+  const int64_t t = q_begin + i0 + (ok ? tok : 0);
+  T::qop_t qop[T::kQSteps];
+  T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+  const int nb = (int)((q_begin + i0 + ntok - 1) / kBlock) + 1;  // blocks 0 .. local of the last
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 o[4] = {};
+
+  for (int c = 0; c < nb; ++c) {
+    if (c > 0) __syncthreads();  // every wave is done with the previous block
+    int tid_v = tid;  // lane-derived addresses are recomputed per block, not kept live
+    asm volatile("" : "+v"(tid_v));
+    const int lane_v = tid_v & 63;
+    const int n32v = lane_v & 31, qv = lane_v >> 5;
+    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
+    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
+    MSA_WAIT_VMCNT(0);
+    __syncthreads();
+    const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
+    const int limq = lim - 4 * q;
+    const bool causal = __ballot(lim < kBlock - 1) != 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float p[2][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const int kt = 2 * half + kk2;
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sv[r];
+          if (causal) x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
+          p[kk2][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mxs = mx * qk_scale;
+      const bool raise = mxs > m_run + 8.f;  // key 0 of block 0 is visible to every row
+      if (__ballot(raise)) {
+        const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
+        m_run = raise ? mxs : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ev = fast_exp2(fmaf(p[kk2][r], qk_scale, -m_run));
+          p[kk2][r] = ev;
+          lsum += ev;
+        }
+      lsum += __shfl_xor(lsum, 32, 64);
+      l_run += lsum;
+      u32x4 pb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* pr = &p[u >> 1][8 * (u & 1)];
+        pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+      }
+      pv_half_tr(o, pb, Vb, lane_v, half);
+    }
+  }
+  if (ok) {
+    const float inv = 1.f / l_run;
+    uint16_t* dst = out + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        T::store4(dst + 32 * dt + 8 * jj + 4 * q, o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv,
+                  o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
+  }
+}
+
+hipError_t launch_dense_prefill_bf16(const void* q, const void* k, const void* v, void* out, int G,
+                                     int Hpg, int64_t q_begin, int64_t q_count, int64_t seq_len,
+                                     hipStream_t st) {
+  const int QT = qtile_tokens(Hpg, 1);
+  const int64_t ntiles = (q_count + QT - 1) / QT;
+  hipLaunchKernelGGL(dense_attn_bf16_kernel, dim3((unsigned)(ntiles * G)), dim3(256), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
+                     G, Hpg, q_begin, q_count, seq_len);
+  return hipGetLastError();
+}
+
 // ---- host side -------------------------------------------------------------------------------
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 

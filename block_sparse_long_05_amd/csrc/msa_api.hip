@@ -257,6 +257,10 @@ msa_status msa_dense_gqa_attn(const msa_problem* p, const void* q, const void* k
     return run_decode_attention(p, true, q, k, v, nullptr, out, workspace, workspace_bytes,
                                 as_stream(stream));
   if (p->q_count == 0) return MSA_OK;
+  if (p->dtype == MSA_DTYPE_BF16)
+    return hip_status(launch_dense_prefill_bf16(q, k, v, out, p->num_groups, p->heads_per_group,
+                                                p->q_begin, p->q_count, p->seq_len,
+                                                as_stream(stream)));
   GatherParams gp = {};
   gp.mode = kPrefillDense;
   gp.bf16 = p->dtype == MSA_DTYPE_BF16;

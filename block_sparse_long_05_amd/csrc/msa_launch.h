@@ -54,6 +54,11 @@ hipError_t launch_decode_combine(int bf16, const float* part_o, const float* par
 // KV-centric sparse prefill attention (attn_tile.hip): reverse index, per-block tiles,
 // log-sum-exp merge. `workspace` must hold kv_workspace_bytes(...) bytes.
 size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, int nblk);
+// Dense causal GQA prefill (bf16, flash-style) for query rows [q_begin, q_begin + q_count).
+hipError_t launch_dense_prefill_bf16(const void* q, const void* k, const void* v, void* out, int G,
+                                     int Hpg, int64_t q_begin, int64_t q_count, int64_t seq_len,
+                                     hipStream_t stream);
+
 hipError_t launch_kv_prefill(int bf16, const void* q, const void* k, const void* v,
                              const int32_t* block_idx, void* out, void* workspace, int G, int Hpg,
                              int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,

@@ -97,6 +97,24 @@ def test_prefill_all_blocks_equals_dense(dtype):
     assert np.max(np.abs(parity.np32(dense) - ref)) <= tol
 
 
+@pytest.mark.parametrize("Hpg,q0,qn", [(8, 0, 1100), (8, 100, 500), (3, 37, 700), (16, 250, 333)])
+def test_dense_prefill_entry_chunks(Hpg, q0, qn):
+    """The dense GQA prefill entry on a query chunk (tiles that straddle block borders,
+    ragged last tile) equals the oracle's dense causal attention on those rows."""
+    T, G = 1100, 2
+    x = synth.prefill_inputs(T, G, Hpg, 128, 64, dtype="bf16", seed=11)
+    ref = orc.dense_prefill(x["q"], x["k"], x["v"])
+    xd = _to(x)
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg, index_dim=64,
+                    top_k=1, seq_len=T, q_begin=q0, q_count=qn)
+    dense = torch.zeros_like(xd["q"])
+    msa.msa_dense_gqa_attn(p, xd["q"], xd["k"], xd["v"], dense)
+    torch.cuda.synchronize()
+    got = parity.np32(dense)
+    assert np.max(np.abs(got[q0:q0 + qn] - ref[q0:q0 + qn])) <= parity.OUT_TOL[x["q"].dtype]
+    assert np.all(got[:q0] == 0) and np.all(got[q0 + qn:] == 0)
+
+
 def _run_decode(x, top_k):
     xd = _to(x)
     out, idx, bs = msa.decode(xd, top_k)
