@@ -71,6 +71,30 @@ def prefill_attn_flops(T, Hq, D, top_k):
     return 4.0 * D * Hq * tot
 
 
+def dense_prefill_flops(T, Hq, D):
+    """Causal dense attention: 4 D FLOPs per (head, query t, visible key j <= t)."""
+    return 4.0 * D * Hq * T * (T + 1) / 2
+
+
+def dense_decode_bytes(lens, G, Hpg, D, esize):
+    """Whole-cache decode: every visible K and V row of each group once, plus q and out."""
+    return sum(2 * G * L * D * esize + 2 * G * Hpg * D * esize for L in lens)
+
+
+def time_reps(torch, fn, reps):
+    """Mean milliseconds of fn() over reps runs after one untimed run (HIP events)."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def decode_bytes(lens, G, Hpg, D, d_idx, top_k, esize):
     tot = 0
     for L in lens:
@@ -238,6 +262,21 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
         f"path {total_tflops:.1f} TFLOP/s ({res['path_frac_of_peak']*100:.1f}% of peak)  "
         f"index {idx_tflops:.1f} TFLOP/s")
+    if args.dense_reps > 0:
+        # dense causal GQA attention over the same rows (the speedup context): same chunks
+        dout = torch.empty_like(q)  # its own output: `out` is checked against the oracle below
+
+        def dense_step():
+            for p in probs:
+                msa.msa_dense_gqa_attn(p, q, x["k"], x["v"], dout)
+        dense_ms = time_reps(torch, dense_step, args.dense_reps)
+        del dout
+        dense_flops = dense_prefill_flops(T, G * Hpg, 128)
+        res["dense"] = dict(ms=dense_ms, tflops=dense_flops / (dense_ms * 1e-3) / 1e12,
+                            frac_of_peak=dense_flops / (dense_ms * 1e-3) / 1e12 / peak,
+                            speedup=dense_ms / ms, reps=args.dense_reps)
+        log(f"[{name}] dense GQA {dense_ms:.1f} ms ({res['dense']['tflops']:.0f} TFLOP/s); "
+            f"MSA speedup {res['dense']['speedup']:.1f}x")
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = prefill_oracle_sample(name, cfg, x, out, idx_full,
                                                                    args)
@@ -358,9 +397,22 @@ def run_decode(name, cfg, args, torch, msa, synth):
                       peak=PEAK_HBM_GBS, unit="GB/s", frac=scan_gbs / PEAK_HBM_GBS,
                       traffic=measured_traffic("index_scores_decode"), work_per_launch=scan_bytes, launch_ms=scan_ms),
     )
+    if args.dense_reps > 0:
+        dws = msa.alloc_workspace(p, "dense_gqa_attn")
+        dout = torch.empty_like(out)  # `out` is checked against the oracle below
+        dense_ms = time_reps(torch, lambda: msa.msa_dense_gqa_attn(p, x["q"], x["k_cache"],
+                                                                    x["v_cache"], dout, dws),
+                             max(3, args.dense_reps))
+        dense_bytes = dense_decode_bytes(lens, G, Hpg, 128, esize)
+        res["dense"] = dict(us_per_step=dense_ms * 1e3, gbs=dense_bytes / (dense_ms * 1e-3) / 1e9,
+                            frac_of_hbm=dense_bytes / (dense_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            speedup=dense_ms / ms_plain)
+        del dws, dout
     log(f"[{name}] {res['us_per_step']:.1f} us/step {res['us_per_token']:.2f} us/token  "
         f"kernels {res['kernel_us']}  path {res['path_gbs']:.0f} GB/s "
-        f"({res['path_frac_of_hbm']*100:.1f}% of HBM)  scan {scan_gbs:.0f} GB/s")
+        f"({res['path_frac_of_hbm']*100:.1f}% of HBM)  scan {scan_gbs:.0f} GB/s"
+        + (f"  dense {res['dense']['us_per_step']:.0f} us/step, MSA speedup "
+           f"{res['dense']['speedup']:.1f}x" if "dense" in res else ""))
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = decode_oracle_sample(name, cfg, x, out, idx, args,
                                                                   torch)
@@ -418,6 +470,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefill query rows per call (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-reps", type=int, default=1,
+                    help="timed runs of the dense GQA entry point on the same workload "
+                         "(speedup context; 0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
