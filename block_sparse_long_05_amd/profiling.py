@@ -4,6 +4,7 @@ traffic table bench.py reports).
     python -m block_sparse_long_05_amd.profiling stats <kernel_stats.csv> [--cmd "..."]
     python -m block_sparse_long_05_amd.profiling traffic --fetch <dir> --write <dir>
             --copy-mib N --out <traffic.json> [--cmd "..."]
+    python -m block_sparse_long_05_amd.profiling traffic-text <traffic.json> [--workloads "..."]
 
 `traffic` reads the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) taken with bench.py --copy-calibration-mib N, scales each
@@ -31,9 +32,10 @@ KERNEL_SOURCES = {
     "index_scores_decode": "index_scores.hip",
     "block_topk": "block_topk.hip",
     "kv_": "attn_tile.hip",
+    "qtile_attn": "attn_tile.hip",
+    "dense_attn": "attn_tile.hip",
     "gather_attn": "attn_gather.hip",
     "decode_combine": "attn_gather.hip",
-    "dense_": "attn_dense.hip",
 }
 
 
@@ -112,6 +114,22 @@ def traffic(fetch_dir: str, write_dir: str, copy_mib: float, cmd: str = "") -> d
                 kernels=kernels)
 
 
+def traffic_text(t: dict, workloads: str = "") -> str:
+    out = ["HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (two runs),",
+           f"scaled by the same counters for a plain {t['copy_mib']:.0f} MiB device copy: "
+           f"fetch x{t['fetch_scale']:.3f}, write x{t['write_scale']:.3f}"]
+    if t.get("command"):
+        out.append(f"command: {t['command']}")
+    if workloads:
+        out.append(f"workloads: {workloads}")
+    out += ["", f"{'read_GB':>10} {'write_GB':>10}  kernel"]
+    rows = sorted(t["kernels"].items(), key=lambda kv: -((kv[1]["read_bytes"] or 0) +
+                                                       (kv[1]["write_bytes"] or 0)))
+    for name, v in rows:
+        out.append(f"{(v['read_bytes'] or 0) / 1e9:10.3f} {(v['write_bytes'] or 0) / 1e9:10.3f}  {name}")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -124,9 +142,14 @@ def main():
     b.add_argument("--copy-mib", type=float, required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--cmd", default="")
+    c = sub.add_parser("traffic-text")
+    c.add_argument("json")
+    c.add_argument("--workloads", default="")
     args = ap.parse_args()
     if args.what == "stats":
         print(stats_text(args.csv, args.cmd), end="")
+    elif args.what == "traffic-text":
+        print(traffic_text(json.load(open(args.json)), args.workloads), end="")
     else:
         t = traffic(args.fetch, args.write, args.copy_mib, args.cmd)
         with open(args.out, "w") as f:
