@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_kernel(
 // LDS block whose 16-byte chunks are XOR-swizzled by row (position p of row r holds
 // chunk p ^ (r % 16)): a quarter-wave loads one whole key row (coalesced) and the MFMA
 // operand reads of 8 rows at a time fall in distinct banks. Each K operand read feeds
-// the 4 row tiles. Block maxima are kept for a few blocks and written together.
+// the 4 row tiles. Block maxima are staged in LDS and written 8 blocks (32 contiguous bytes)
+// per row.
 template <int DI>
 struct PrefillLds {
   static constexpr int kRowBytes = DI * 2;                 // one key row in LDS
@@ -193,7 +194,9 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_lds_kernel(
     float* __restrict__ block_scores, int64_t q_begin, int64_t q_count, int G, int top_k,
     int nblk) {
   typedef PrefillLds<DI> C;
+  constexpr int kBatch = 8;  // blocks whose maxima are written together (32 B per row)
   __shared__ __align__(16) uint8_t lds[2][C::kBufBytes];
+  __shared__ __align__(16) float stage[4][128][kBatch];  // per wave: its rows x the batch
   constexpr int kRows = 512;  // rows per workgroup
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -215,26 +218,15 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_lds_kernel(
     for (int s = 0; s < C::kSteps; ++s)
       qop[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
   }
-  // Rows this lane writes: tiles 2*q and 2*q + 1 at column lane % 32.
-  int64_t Rw[2];
-  int bw[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    Rw[j] = r0 + 128 * wave + 32 * (2 * q + j) + (lane & 31);
-    bw[j] = Rw[j] < nrows ? (int)((q_begin + Rw[j] / G) / kBlock) : -1;
-    if (bw[j] < top_k) bw[j] = 0;  // rows keeping all their blocks write nothing
-  }
+  const bool vec_ok = (nblk & 3) == 0;  // 16-byte row pieces of block_scores are aligned
 
   prefill_issue_block<DI>(k_idx, 0, lds[0], wave, lane);
   MSA_WAIT_VMCNT(0);
   __syncthreads();
-  constexpr int kBatch = DI == 128 ? 4 : 8;  // blocks whose maxima are written together
   for (int cb = 0; cb < cmax; cb += kBatch) {
-    float outv[2][kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int c = cb + j;
-      outv[0][j] = outv[1][j] = 0.f;
       if (c < cmax) {
         const bool has_next = c + 1 < cmax;
         if (has_next) prefill_issue_block<DI>(k_idx, c + 1, lds[(c + 1) & 1], wave, lane);
@@ -258,19 +250,40 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_lds_kernel(
         }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
-        outv[0][j] = q == 0 ? mx[0] : mx[2];
-        outv[1][j] = q == 0 ? mx[1] : mx[3];
+        // tiles 2q and 2q + 1 go to the stage from this half (column lane % 32)
+        stage[wave][32 * (2 * q) + (lane & 31)][j] = q == 0 ? mx[0] : mx[2];
+        stage[wave][32 * (2 * q + 1) + (lane & 31)][j] = q == 0 ? mx[1] : mx[3];
         if (has_next) MSA_WAIT_VMCNT(0);  // this wave's part of block c + 1 has landed
         __syncthreads();
       }
     }
+    // The wave's 128 rows x kBatch maxima leave as 16-byte pieces (4 per lane), each row's
+    // run contiguous; only blocks c < b(row) (and c < cmax) are written, and nothing for
+    // rows that keep all their blocks.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage writes are done
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int rj = 0; rj < 2; ++rj) {
-      float* orow = block_scores + (Rw[rj] < nrows ? Rw[rj] : 0) * (int64_t)nblk;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        if (cb + j < bw[rj]) orow[cb + j] = outv[rj][j];
+    for (int it = 0; it < 4; ++it) {
+      const int piece = 64 * it + lane;
+      const int row = piece >> 1, hf = piece & 1;
+      const int64_t R = r0 + 128 * wave + row;
+      int lim = R < nrows ? (int)((q_begin + R / G) / kBlock) : 0;
+      if (lim < top_k) lim = 0;
+      lim = min(lim, cmax);
+      const float4 v = *reinterpret_cast<const float4*>(&stage[wave][row][4 * hf]);
+      const int c0 = cb + 4 * hf;
+      float* dst = block_scores + (R < nrows ? R : 0) * (int64_t)nblk + c0;
+      if (vec_ok && c0 + 3 < lim) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        if (c0 + 0 < lim) dst[0] = v.x;
+        if (c0 + 1 < lim) dst[1] = v.y;
+        if (c0 + 2 < lim) dst[2] = v.z;
+        if (c0 + 3 < lim) dst[3] = v.w;
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the stage reads are done before it is reused
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
