@@ -200,7 +200,9 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     probs = [msa.Problem(dtype=cfg["dtype"], mode="prefill", num_groups=G, heads_per_group=Hpg,
                          index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n,
                          algo=args.algo) for c0, n in chunks]
-    bs = torch.empty((chunk, G, probs[0].nblk), dtype=torch.float32, device="cuda")
+    fused = args.index == "fused" and all(msa.index_topk_supported(p) for p in probs)
+    bs = None if fused else torch.empty((chunk, G, probs[0].nblk), dtype=torch.float32,
+                                        device="cuda")
     idx_full = torch.empty((T, G, top_k), dtype=torch.int32, device="cuda")
     ws_bytes = max(msa.msa_workspace_size(p, "sparse_attn_prefill") for p in probs)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes else None
@@ -211,14 +213,21 @@ def run_prefill(name, cfg, args, torch, msa, synth):
         for p, (c0, n) in zip(probs, chunks):
             idx = idx_full[c0:c0 + n]
             if not timed:
-                msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
-                msa.msa_block_topk(p, bs, idx)
+                if fused:
+                    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
+                else:
+                    msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+                    msa.msa_block_topk(p, bs, idx)
                 msa.msa_sparse_attn_prefill(p, q, x["k"], x["v"], idx, out, ws)
                 continue
-            with timers.setdefault("index_scores", KernelTimer(torch)):
-                msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
-            with timers.setdefault("block_topk", KernelTimer(torch)):
-                msa.msa_block_topk(p, bs, idx)
+            if fused:
+                with timers.setdefault("index_topk", KernelTimer(torch)):
+                    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
+            else:
+                with timers.setdefault("index_scores", KernelTimer(torch)):
+                    msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
+                with timers.setdefault("block_topk", KernelTimer(torch)):
+                    msa.msa_block_topk(p, bs, idx)
             with timers.setdefault("sparse_attn", KernelTimer(torch)):
                 msa.msa_sparse_attn_prefill(p, q, x["k"], x["v"], idx, out, ws)
 
@@ -245,18 +254,22 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     idx_flops = prefill_index_flops(T, G, d_idx, top_k)
     att_flops = prefill_attn_flops(T, G * Hpg, 128, top_k)
     peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
-    idx_ms_launch = timers["index_scores"].mean_ms()
+    idx_name = "index_topk" if fused else "index_scores"
+    idx_ms_launch = timers[idx_name].mean_ms()
     idx_tflops = idx_flops / len(chunks) / (idx_ms_launch * 1e-3) / 1e12
     total_tflops = (idx_flops + att_flops) / (ms * 1e-3) / 1e12
     res = dict(
         workload=name, T=T, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
-        chunk=chunk, algo=args.algo, ms_per_step=ms, wall_s=wall, tok_per_s=T / (ms * 1e-3),
+        chunk=chunk, algo=args.algo, index_branch="fused" if fused else "separate",
+        ms_per_step=ms, wall_s=wall, tok_per_s=T / (ms * 1e-3),
         kernel_ms_per_step=per_kernel,
         flops=dict(index=idx_flops, attention=att_flops),
         path_tflops=total_tflops, path_frac_of_peak=total_tflops / peak,
-        roofline=dict(bound="mfma", kernel="index_scores_prefill", achieved=idx_tflops,
-                      peak=peak, unit="TFLOP/s", frac=idx_tflops / peak,
-                      traffic=measured_traffic("index_scores_prefill"),
+        roofline=dict(bound="mfma",
+                      kernel="index_topk_prefill" if fused else "index_scores_prefill",
+                      achieved=idx_tflops, peak=peak, unit="TFLOP/s", frac=idx_tflops / peak,
+                      traffic=measured_traffic("index_topk_prefill" if fused
+                                               else "index_scores_prefill"),
                       work_per_launch=idx_flops / len(chunks), launch_ms=idx_ms_launch),
     )
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
@@ -464,6 +477,9 @@ def main():
     ap.add_argument("--prefill", default="prefill_128k", help="prefill workload ('none' to skip)")
     ap.add_argument("--decode", default="decode_1m", help="decode workload ('none' to skip)")
     ap.add_argument("--algo", default="auto", choices=["auto", "query_centric", "kv_centric"])
+    ap.add_argument("--index", default="fused", choices=["fused", "separate"],
+                    help="prefill index branch: one fused index->top-k kernel (when built for "
+                         "the problem) or index scores then top-k")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (the reference "
                          "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")

@@ -288,6 +288,139 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_lds_kernel(
 }
 
 // ------------------------------------------------------------------------------------
+// Fused index -> top-k (prefill, bf16, top_k <= 16)
+// ------------------------------------------------------------------------------------
+// The sweep of the prefill index kernel with 2 row tiles per wave, so that after the block
+// maximum each lane owns one query row (row tile q, column lane % 32). The row keeps its
+// running top-15 (order-preserving key, block id) sorted in registers, key descending and
+// equal keys in arrival order, i.e. ascending id: a block enters only when its key beats
+// the 15th strictly, since an equal key arrived earlier with a lower id and wins the tie.
+// A row's top-(k-1) is contained in its top-15, so the first k-1 entries are its choice
+// (researchpapers.dev summary "Mechanism"; mlqm.cn blog section 2.1). At the end the local
+// block joins and the ids are written ascending. No block score reaches memory.
+constexpr int kFuseK = 15;
+
+template <int DI>
+__global__ __launch_bounds__(256, 2) void index_topk_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    int32_t* __restrict__ block_idx, int64_t q_begin, int64_t q_count, int G, int top_k) {
+  typedef PrefillLds<DI> C;
+  constexpr int RT = 2;
+  constexpr int kRows = 128 * RT;  // rows per workgroup
+  __shared__ __align__(16) uint8_t lds[2][C::kBufBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 5;
+  const int64_t nrows = q_count * G;
+  const int64_t r0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * kRows;  // heaviest rows first
+  const int64_t r_last = min(r0 + kRows - 1, nrows - 1);
+  const int cmax = (int)((q_begin + r_last / G) / kBlock);  // blocks swept: 0 .. cmax - 1
+  const int64_t R = r0 + 32 * RT * wave + 32 * q + (lane & 31);   // this lane's row
+  const bool own = R < nrows;
+  const int b = own ? (int)((q_begin + R / G) / kBlock) : 0;     // its local block
+
+  uint32_t tk[kFuseK];
+  int32_t ti[kFuseK];
+#pragma unroll
+  for (int i = 0; i < kFuseK; ++i) {
+    tk[i] = 0u;  // below the key of every finite float
+    ti[i] = -1;
+  }
+  if (cmax >= top_k) {  // some row of the workgroup ranks blocks
+    u32x4 qop[RT][C::kSteps];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int64_t Rq = r0 + 32 * RT * wave + 32 * rt + (lane & 31);
+      const bool ok = Rq < nrows;
+      const uint16_t* qp = q_idx + (q_begin * G + (ok ? Rq : 0)) * DI + 8 * q;
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s)
+        qop[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+    }
+    prefill_issue_block<DI>(k_idx, 0, lds[0], wave, lane);
+    MSA_WAIT_VMCNT(0);
+    __syncthreads();
+    for (int c = 0; c < cmax; ++c) {
+      const bool has_next = c + 1 < cmax;
+      if (has_next) prefill_issue_block<DI>(k_idx, c + 1, lds[(c + 1) & 1], wave, lane);
+      const uint8_t* kb = lds[c & 1];
+      float mx[RT] = {-INFINITY, -INFINITY};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int m = 32 * kt + (lane & 31);
+        f32x16 acc[RT] = {};
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) {
+          const int pos = (2 * s + q) ^ (m & (C::kChunks - 1));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kb + m * C::kRowBytes + pos * 16);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a, qop[rt][s], acc[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx[rt] = fmaxf(mx[rt], fmaxf(acc[rt][r], acc[rt][r + 1]));
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
+      const uint32_t key = ordered_key(q == 0 ? mx[0] : mx[1]);
+      if (c < b && key > tk[kFuseK - 1]) {
+        // sorted insert (old values are read before they are overwritten: i descends)
+#pragma unroll
+        for (int i = kFuseK - 1; i > 0; --i) {
+          const bool up = key > tk[i - 1];
+          const bool at = key > tk[i];
+          tk[i] = up ? tk[i - 1] : (at ? key : tk[i]);
+          ti[i] = up ? ti[i - 1] : (at ? c : ti[i]);
+        }
+        if (key > tk[0]) {
+          tk[0] = key;
+          ti[0] = c;
+        }
+      }
+      if (has_next) MSA_WAIT_VMCNT(0);  // this wave's part of block c + 1 has landed
+      __syncthreads();
+    }
+  }
+  if (!own) return;
+  int32_t* o = block_idx + R * top_k;
+  if (b + 1 <= top_k) {  // every visible block is kept
+    for (int i = 0; i < top_k; ++i) o[i] = i <= b ? i : -1;
+    return;
+  }
+  // the first K = top_k - 1 entries, ascending (odd-even transposition sort), then b
+  const int K = top_k - 1;
+  int32_t sel[kFuseK];
+#pragma unroll
+  for (int i = 0; i < kFuseK; ++i) sel[i] = i < K ? ti[i] : 0x7fffffff;
+#pragma unroll
+  for (int round = 0; round < kFuseK; ++round)
+#pragma unroll
+    for (int i = round & 1; i + 1 < kFuseK; i += 2) {
+      const int32_t lo = min(sel[i], sel[i + 1]), hi = max(sel[i], sel[i + 1]);
+      sel[i] = lo;
+      sel[i + 1] = hi;
+    }
+  for (int i = 0; i < K; ++i) o[i] = sel[i];
+  o[K] = b;
+}
+
+hipError_t launch_index_topk_prefill(int index_dim, const void* q_idx, const void* k_idx,
+                                     int32_t* block_idx, int64_t q_begin, int64_t q_count, int G,
+                                     int top_k, hipStream_t st) {
+  const int64_t grid = (q_count * G + 255) / 256;
+  if (index_dim == 128)
+    hipLaunchKernelGGL(index_topk_prefill_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, block_idx, q_begin,
+                       q_count, G, top_k);
+  else
+    hipLaunchKernelGGL(index_topk_prefill_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, block_idx, q_begin,
+                       q_count, G, top_k);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
 // Decode
 // ------------------------------------------------------------------------------------
 template <class E, int DI>

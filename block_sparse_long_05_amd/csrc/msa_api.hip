@@ -142,6 +142,7 @@ msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes
   switch (entry) {
     case MSA_ENTRY_INDEX_SCORES:
     case MSA_ENTRY_BLOCK_TOPK:
+    case MSA_ENTRY_INDEX_TOPK:
       return MSA_OK;
     case MSA_ENTRY_SPARSE_ATTN_PREFILL:
       if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
@@ -189,6 +190,20 @@ msa_status msa_block_topk(const msa_problem* p, const float* block_scores, int32
   return hip_status(launch_block_topk(block_scores, block_idx, rows, p->num_groups,
                                       (int)nblk_of(p), p->top_k, decode ? 1 : 0, p->q_begin,
                                       p->seq_lens, p->max_len, as_stream(stream)));
+}
+
+msa_status msa_index_topk(const msa_problem* p, const void* q_idx, const void* k_idx,
+                          int32_t* block_idx, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_PREFILL || p->dtype != MSA_DTYPE_BF16 || p->top_k > 16)
+    return MSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(block_idx))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->q_count == 0) return MSA_OK;
+  return hip_status(launch_index_topk_prefill(p->index_dim, q_idx, k_idx, block_idx, p->q_begin,
+                                              p->q_count, p->num_groups, p->top_k,
+                                              as_stream(stream)));
 }
 
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,

@@ -18,6 +18,11 @@ hipError_t launch_index_scores_decode(int bf16, int index_dim, const void* q_idx
                                       const int32_t* seq_lens, int B, int64_t max_len, int G,
                                       int top_k, int nblk, hipStream_t stream);
 
+// Fused prefill index scores + block max + top-k (bf16, top_k <= 16).
+hipError_t launch_index_topk_prefill(int index_dim, const void* q_idx, const void* k_idx,
+                                     int32_t* block_idx, int64_t q_begin, int64_t q_count, int G,
+                                     int top_k, hipStream_t stream);
+
 hipError_t launch_block_topk(const float* block_scores, int32_t* block_idx, int64_t rows, int G,
                              int nblk, int top_k, int decode, int64_t q_begin,
                              const int32_t* seq_lens, int64_t max_len, hipStream_t stream);

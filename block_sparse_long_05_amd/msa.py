@@ -26,13 +26,13 @@ MSA_ERR_HIP = 4
 DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"prefill": 0, "decode": 1}
 ENTRY = {"index_scores": 0, "block_topk": 1, "sparse_attn_prefill": 2,
-         "sparse_attn_decode": 3, "dense_gqa_attn": 4}
+         "sparse_attn_decode": 3, "dense_gqa_attn": 4, "index_topk": 5}
 ALGO = {"auto": 0, "query_centric": 1, "kv_centric": 2}
 
 BLOCK = 128
 
 # Every symbol include/msa.h declares.
-EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_sparse_attn_prefill",
+EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
             "msa_status_string", "msa_abi_version"]
 
@@ -70,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     pp = ctypes.POINTER(CProblem)
     lib.msa_index_scores.argtypes = [pp, vp, vp, vp, vp]
     lib.msa_block_topk.argtypes = [pp, vp, vp, vp]
+    lib.msa_index_topk.argtypes = [pp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
@@ -77,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_abi_version.argtypes = []
-    for name in ("msa_index_scores", "msa_block_topk", "msa_sparse_attn_prefill",
+    for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
                  "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
                  "msa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -172,6 +173,16 @@ def msa_block_topk(p: Problem, block_scores, block_idx, stream=None):
                                          _stream(stream)), "msa_block_topk")
 
 
+def msa_index_topk(p: Problem, q_idx, k_idx, block_idx, stream=None):
+    _check(load_library().msa_index_topk(ctypes.byref(p.c()), _ptr(q_idx), _ptr(k_idx),
+                                         _ptr(block_idx), _stream(stream)), "msa_index_topk")
+
+
+def index_topk_supported(p: Problem) -> bool:
+    """Whether msa_index_topk (the fused index branch) is built for this problem."""
+    return p.mode == "prefill" and p.dtype == "bf16" and p.top_k <= 16
+
+
 def msa_sparse_attn_prefill(p: Problem, q, k, v, block_idx, out, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().msa_sparse_attn_prefill(
@@ -215,10 +226,11 @@ def alloc_block_idx(p: Problem, device="cuda") -> torch.Tensor:
 
 def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None,
             algo: str = "auto", out=None, block_scores=None, block_idx=None, workspace=None,
-            stream=None):
+            stream=None, index: str = "separate"):
     """MSA prefill of query rows [q_begin, q_begin + q_count): index scores -> top-k ->
-    sparse attention. x holds q, k, v, q_idx, k_idx on the device. Returns
-    (out, block_idx, block_scores)."""
+    sparse attention. x holds q, k, v, q_idx, k_idx on the device. index="fused" runs the
+    index branch as msa_index_topk (no block scores; block_scores is returned as None).
+    Returns (out, block_idx, block_scores)."""
     q = x["q"]
     T, Hq, D = q.shape
     G = x["k"].shape[0]
@@ -227,16 +239,22 @@ def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None
     p = Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="prefill",
                 num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
                 top_k=top_k, head_dim=D, seq_len=T, q_begin=q_begin, q_count=q_count, algo=algo)
+    if index not in ("separate", "fused"):
+        raise ValueError(f"index must be 'separate' or 'fused', not {index!r}")
     if out is None:
         out = torch.empty_like(q)
-    if block_scores is None:
-        block_scores = alloc_block_scores(p, q.device)
     if block_idx is None:
         block_idx = alloc_block_idx(p, q.device)
     if workspace is None:
         workspace = alloc_workspace(p, "sparse_attn_prefill", q.device)
-    msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
-    msa_block_topk(p, block_scores, block_idx, stream)
+    if index == "fused":
+        msa_index_topk(p, x["q_idx"], x["k_idx"], block_idx, stream)
+        block_scores = None
+    else:
+        if block_scores is None:
+            block_scores = alloc_block_scores(p, q.device)
+        msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
+        msa_block_topk(p, block_scores, block_idx, stream)
     msa_sparse_attn_prefill(p, q, x["k"], x["v"], block_idx, out, workspace, stream)
     return out, block_idx, block_scores
 

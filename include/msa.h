@@ -67,7 +67,8 @@ typedef enum {
   MSA_ENTRY_BLOCK_TOPK = 1,
   MSA_ENTRY_SPARSE_ATTN_PREFILL = 2,
   MSA_ENTRY_SPARSE_ATTN_DECODE = 3,
-  MSA_ENTRY_DENSE_GQA_ATTN = 4
+  MSA_ENTRY_DENSE_GQA_ATTN = 4,
+  MSA_ENTRY_INDEX_TOPK = 5
 } msa_entry;
 
 /* Prefill main-branch algorithm. Both give the same result up to fp32 rounding. */
@@ -121,6 +122,18 @@ msa_status msa_index_scores(const msa_problem* p, const void* q_idx, const void*
  */
 msa_status msa_block_topk(const msa_problem* p, const float* block_scores, int32_t* block_idx,
                           void* stream);
+
+/*
+ * Index branch, steps 1-3 fused (prefill): writes block_idx for query rows
+ * [q_begin, q_begin + q_count) exactly as msa_index_scores followed by msa_block_topk
+ * would, but the block scores never reach memory: each query row keeps a running
+ * top-(k-1) of its block maxima while the key blocks stream past (researchpapers.dev
+ * summary "Mechanism"; mlqm.cn blog, section 2.1). Same ranking, padding and layout as
+ * msa_block_topk. Built for dtype bf16, top_k <= 16 and prefill; any other problem returns
+ * MSA_ERR_UNSUPPORTED (the two separate calls cover it). No workspace.
+ */
+msa_status msa_index_topk(const msa_problem* p, const void* q_idx, const void* k_idx,
+                          int32_t* block_idx, void* stream);
 
 /*
  * Main branch, prefill (mlqm.cn blog, section 2.2: gather the kept K/V blocks, then

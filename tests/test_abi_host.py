@@ -142,3 +142,22 @@ def test_empty_chunk_is_a_no_op():
     assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_OK
     assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0) \
         == msa.MSA_OK
+
+
+def test_index_topk_rejections():
+    """The fused index branch is built for bf16 prefill with top_k <= 16 only; anything
+    else is refused on the host (MSA_ERR_UNSUPPORTED), as are misaligned pointers."""
+    lib = msa.load_library()
+    ok = _prefill(top_k=16)
+    assert msa.index_topk_supported(ok)
+    for p in (_prefill(dtype="f32"), _prefill(top_k=17)):
+        assert not msa.index_topk_supported(p)
+        assert lib.msa_index_topk(ctypes.byref(p.c()), FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_topk(ctypes.byref(_decode()), FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_topk(ctypes.byref(ok.c()), FAKE + 4, FAKE, FAKE, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_index_topk(ctypes.byref(_prefill(q_begin=4096, q_count=0).c()), FAKE, FAKE,
+                              FAKE, 0) == msa.MSA_OK
+    n = ctypes.c_size_t(7)
+    assert lib.msa_workspace_size(ctypes.byref(ok.c()), msa.ENTRY["index_topk"],
+                                  ctypes.byref(n)) == msa.MSA_OK and n.value == 0

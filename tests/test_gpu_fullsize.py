@@ -48,7 +48,13 @@ def test_prefill_128k_sampled_rows():
     x = synth.prefill_inputs(T, 8, 8, 128, 128, dtype="bf16", seed=1000 + T,
                              planted_per_group=8, device="cuda")
     out, idx, _ = msa.prefill(x, 16)
+    # the fused index branch (the launch bench.py times) selects exactly the same blocks
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=8, heads_per_group=8,
+                    index_dim=128, top_k=16, seq_len=T, q_begin=0, q_count=T)
+    fused = msa.alloc_block_idx(p)
+    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], fused)
     torch.cuda.synchronize()
+    assert torch.equal(fused, idx)
     host = {k: x[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
     for lo in (0, 2048 + 17, 65536 - 16, T - 32):
         rows = np.arange(lo, min(lo + 32, T))

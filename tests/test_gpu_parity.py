@@ -115,6 +115,53 @@ def test_dense_prefill_entry_chunks(Hpg, q0, qn):
     assert np.all(got[:q0] == 0) and np.all(got[q0 + qn:] == 0)
 
 
+FUSED_CASES = [c for c in PREFILL_CASES if c[5] == "bf16" and c[4] <= 16] + [
+    (3000, 2, 4, 128, 16, "bf16", 0),   # random scores (near ties possible), 24 blocks
+    (2600, 3, 2, 64, 9, "bf16", 5),     # index dim 64, top_k between 1 and 16
+]
+
+
+@pytest.mark.parametrize("T,G,Hpg,d_idx,top_k,dtype,planted", FUSED_CASES)
+def test_index_topk_fused(T, G, Hpg, d_idx, top_k, dtype, planted):
+    """msa_index_topk equals msa_index_scores + msa_block_topk bit for bit (same block
+    maxima, same ranking), and both match the oracle's selection up to declared near ties."""
+    x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype=dtype, seed=T + 3 * G,
+                             planted_per_group=planted)
+    print(f"fused index-topk T={T} G={G} d_idx={d_idx} k={top_k}", flush=True)
+    xd = _to(x)
+    for q0, qn in ((0, T), (T // 3 + 5, T // 2)):
+        p = msa.Problem(dtype=dtype, mode="prefill", num_groups=G, heads_per_group=Hpg,
+                        index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=q0, q_count=qn)
+        assert msa.index_topk_supported(p)
+        fused = torch.full((qn, G, top_k), -7, dtype=torch.int32, device="cuda")
+        msa.msa_index_topk(p, xd["q_idx"], xd["k_idx"], fused)
+        bs = msa.alloc_block_scores(p)
+        sep = msa.alloc_block_idx(p)
+        msa.msa_index_scores(p, xd["q_idx"], xd["k_idx"], bs)
+        msa.msa_block_topk(p, bs, sep)
+        torch.cuda.synchronize()
+        assert torch.equal(fused, sep)
+    rows = np.arange(T)
+    res = _oracle_prefill(("fused", T, G, Hpg, d_idx, top_k, dtype, planted), x, top_k, rows=rows)
+    p = msa.Problem(dtype=dtype, mode="prefill", num_groups=G, heads_per_group=Hpg,
+                    index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=0, q_count=T)
+    fused = msa.alloc_block_idx(p)
+    msa.msa_index_topk(p, xd["q_idx"], xd["k_idx"], fused)
+    torch.cuda.synchronize()
+    parity.check_selection(fused.cpu().numpy(), res["sel"], res["near_tie"], top_k, label="fused")
+
+
+def test_prefill_pipeline_fused_index():
+    """The whole prefill with the fused index branch gives the separate path's output."""
+    T, G, Hpg = 2300, 4, 8
+    x = _to(synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=41, planted_per_group=4))
+    a_out, a_idx, _ = msa.prefill(x, 16)
+    b_out, b_idx, b_bs = msa.prefill(x, 16, index="fused")
+    torch.cuda.synchronize()
+    assert b_bs is None
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_out, b_out)
+
+
 def _run_decode(x, top_k):
     xd = _to(x)
     out, idx, bs = msa.decode(xd, top_k)
