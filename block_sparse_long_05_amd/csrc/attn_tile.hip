@@ -139,18 +139,28 @@ __global__ void kv_count_kernel(const int32_t* __restrict__ block_idx, int64_t n
   }
 }
 
-// Exclusive scan over (bucket, stripe) in bucket-major order. Writes cursor[] (same
-// layout as count[]) and bucket_off[0..nb] (start of each bucket; bucket_off[nb] = total).
-__global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict__ count,
-                                                       int64_t nb, int32_t* __restrict__ cursor,
-                                                       int32_t* __restrict__ bucket_off) {
+// Exclusive scan over (bucket, stripe) in bucket-major order, in three passes that each
+// read the counters coalesced (one thread per bucket): bucket totals into bucket_off[k],
+// an in-place exclusive scan of the totals (bucket_off[nb] = total), then each stripe's
+// cursor = its bucket's start + the counts of the earlier stripes of that bucket.
+__global__ void kv_bucket_total_kernel(const int32_t* __restrict__ count, int64_t nb,
+                                       int32_t* __restrict__ bucket_off) {
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < nb;
+       k += (int64_t)gridDim.x * blockDim.x) {
+    int32_t s = 0;
+#pragma unroll
+    for (int st = 0; st < kStripes; ++st) s += count[st * nb + k];
+    bucket_off[k] = s;
+  }
+}
+
+__global__ __launch_bounds__(1024) void kv_scan_kernel(int64_t nb, int32_t* __restrict__ bucket_off) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int64_t per = (nb + 1023) / 1024;
   const int64_t lo = min(nb, tid * per), hi = min(nb, lo + per);
   int32_t s = 0;
-  for (int64_t k = lo; k < hi; ++k)
-    for (int st = 0; st < kStripes; ++st) s += count[st * nb + k];
+  for (int64_t k = lo; k < hi; ++k) s += bucket_off[k];
   part[tid] = s;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -161,13 +171,25 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(const int32_t* __restrict
   }
   int32_t run = part[tid] - s;  // exclusive prefix of this thread's range
   for (int64_t k = lo; k < hi; ++k) {
+    const int32_t c = bucket_off[k];
     bucket_off[k] = run;
+    run += c;
+  }
+  if (tid == 1023) bucket_off[nb] = part[1023];
+}
+
+__global__ void kv_cursor_kernel(const int32_t* __restrict__ count, int64_t nb,
+                                 const int32_t* __restrict__ bucket_off,
+                                 int32_t* __restrict__ cursor) {
+  for (int64_t k = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; k < nb;
+       k += (int64_t)gridDim.x * blockDim.x) {
+    int32_t run = bucket_off[k];
+#pragma unroll
     for (int st = 0; st < kStripes; ++st) {
       cursor[st * nb + k] = run;
       run += count[st * nb + k];
     }
   }
-  if (tid == 1023) bucket_off[nb] = part[1023];
 }
 
 __global__ void kv_scatter_kernel(const int32_t* __restrict__ block_idx, int64_t n_entries, int G,
@@ -1396,7 +1418,10 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
                      block_idx, shared, G, top_k, q_begin, q_count, QT, npairs);
   hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
                      top_k, q_begin, nblk, shared, QT, count);
-  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, st, count, nb, cursor, offset);
+  const unsigned grid_b = (unsigned)std::min<int64_t>((nb + 255) / 256, 65536);
+  hipLaunchKernelGGL(kv_bucket_total_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset);
+  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, st, nb, offset);
+  hipLaunchKernelGGL(kv_cursor_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset, cursor);
   hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
                      top_k, q_begin, nblk, shared, QT, cursor, sorted);
   const unsigned tiles = (unsigned)((n_entries + kTile - 1) / kTile);
