@@ -51,9 +51,10 @@ __global__ void kv_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 __device__ __forceinline__ int frag_pos(int dt, int jj, int q) { return 64 * q + 16 * dt + 4 * jj; }
 
 // Query tiles: the rows of one 32-row MFMA tile are floor(32 / Hpg) tokens x Hpg heads,
-// and a query tile is the row tiles of one workgroup (4 for bf16, 8 for fp32).
+// and a query tile is the 8 row tiles of one workgroup.
 __host__ __device__ __forceinline__ int qtile_tokens(int Hpg, int bf16) {
-  return (bf16 ? 4 : 8) * (32 / Hpg);
+  (void)bf16;
+  return 8 * (32 / Hpg);
 }
 
 // True when block c is in the tile's shared list (ascending, -1 padded).
@@ -1053,31 +1054,36 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
 // the block are masked, the local block gets the causal mask. Then each row folds in
 // the partials (o / l, m, l) of its rare entries, computed by the reverse-index path, in
 // slot order, and the final output is written. No partial is stored for shared entries.
-// bf16 form: 4 waves with one row tile each (a query tile is 4 row tiles) and about 66 KB
-// of LDS, so two workgroups share a CU: while one stages a block or reads partials, the
-// other keeps the matrix cores busy. K and V are both staged row-major by direct
-// global->LDS loads; PV reads V through the LDS transpose read. Q stays in registers across the shared blocks. A
+// bf16 form: 8 waves with one row tile each (a query tile is 8 row tiles), one workgroup
+// per CU with the shared blocks double-buffered in LDS: block j + 1 is loaded (K and V
+// row-major, by direct global->LDS loads) while block j is used; PV reads V through the
+// LDS transpose read. Q stays in registers across the shared blocks. A
 // row's running maximum is raised only when a new score exceeds it by more than 8 (log2
 // units), so the accumulator is rescaled rarely and every exponential stays below 2^8;
 // the final division by the row sum makes the result the same up to rounding.
 template <int KMAX>
-__global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
+__global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ shared, const uint16_t* __restrict__ part_o,
     const float* __restrict__ part_ml, uint16_t* __restrict__ out, int G, int Hpg, int top_k,
     int64_t q_begin, int64_t q_count, int64_t seq_len) {
   typedef TileOps<BF16> T;
-  __shared__ __align__(16) uint8_t Kb[kBlock * 256];
-  __shared__ __align__(16) uint8_t Vb[kBlock * 256];
+  // two buffers per operand as distinct arrays: with the block loop unrolled by two every
+  // access names its buffer, so the compiler can tell that the loads of block j + 1 do
+  // not alias the reads of block j (and does not wait for them)
+  __shared__ __align__(16) uint8_t Kb0[kBlock * 256];
+  __shared__ __align__(16) uint8_t Kb1[kBlock * 256];
+  __shared__ __align__(16) uint8_t Vb0[kBlock * 256];
+  __shared__ __align__(16) uint8_t Vb1[kBlock * 256];
   __shared__ int32_t sl[64];
-  __shared__ uint64_t selmask[128];   // per token: which shared blocks it keeps
-  __shared__ uint64_t raremask[128];  // per token: which slots go through the partials
+  __shared__ uint64_t selmask[256];   // per token: which shared blocks it keeps
+  __shared__ uint64_t raremask[256];  // per token: which slots go through the partials
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int epr = 32 / Hpg;
-  const int QT = 4 * epr;
+  const int QT = 8 * epr;
   const int64_t tile = blockIdx.x / G;
   const int g = (int)(blockIdx.x % G);
   const int64_t i0 = tile * QT;
@@ -1126,21 +1132,30 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4] = {};
 
-  for (int j = 0; j < ns; ++j) {
+  if (ns > 0) {
+    const int c0 = __builtin_amdgcn_readfirstlane(sl[0]);
+    k_block_dma<512>(K, g, c0, seq_len, Kb0, tid);
+    k_block_dma<512, true>(V, g, c0, seq_len, Vb0, tid);
+  }
+  auto shared_block = [&](int j, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     const int c = __builtin_amdgcn_readfirstlane(sl[j]);  // uniform: scalar staging base
-    if (j > 0) __syncthreads();  // every wave is done with the previous block
+    // block j (loaded during block j - 1) has landed for every wave, and every wave is
+    // done with block j - 1, whose buffer now takes block j + 1
+    MSA_WAIT_VMCNT(0);
+    __syncthreads();
     // lane-derived addresses are recomputed per block rather than kept live (the empty
     // asm hides that the thread id does not change)
     int tid_v = tid;
     asm volatile("" : "+v"(tid_v));
     const int lane_v = tid_v & 63;
     const int n32v = lane_v & 31, qv = lane_v >> 5;
-    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
-    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
-    MSA_WAIT_VMCNT(0);
-    __syncthreads();
+    if (j + 1 < ns) {
+      const int cn = __builtin_amdgcn_readfirstlane(sl[j + 1]);
+      k_block_dma<512>(K, g, cn, seq_len, Kn, tid_v);
+      k_block_dma<512, true>(V, g, cn, seq_len, Vn, tid_v);
+    }
     const bool sel = (mymask >> j) & 1ull;
-    if (__ballot(sel) == 0) continue;
+    if (__ballot(sel) == 0) return;
     const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
     const int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
     const bool causal = __ballot(sel && lim < kBlock - 1) != 0;
@@ -1152,7 +1167,7 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const int kt = 2 * half + kk2;
-        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+        const f32x16 sv = s_tile_swz(Kc, 32 * kt + n32v, qop, qv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float x = sel ? sv[r] : -INFINITY;
@@ -1194,8 +1209,12 @@ __global__ __launch_bounds__(256, 2) void qtile_attn_bf16_kernel(
         pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
       }
-      pv_half_tr(o, pb, Vb, lane_v, half);
+      pv_half_tr(o, pb, Vc, lane_v, half);
     }
+  };
+  for (int j = 0; j < ns; j += 2) {
+    shared_block(j, Kb0, Vb0, Kb1, Vb1);
+    if (j + 1 < ns) shared_block(j + 1, Kb1, Vb1, Kb0, Vb0);
   }
 
   // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
@@ -1362,7 +1381,7 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16_kernel(
 hipError_t launch_dense_prefill_bf16(const void* q, const void* k, const void* v, void* out, int G,
                                      int Hpg, int64_t q_begin, int64_t q_count, int64_t seq_len,
                                      hipStream_t st) {
-  const int QT = qtile_tokens(Hpg, 1);
+  const int QT = 4 * (32 / Hpg);  // the dense kernel's query tile: 4 row tiles
   const int64_t ntiles = (q_count + QT - 1) / QT;
   hipLaunchKernelGGL(dense_attn_bf16_kernel, dim3((unsigned)(ntiles * G)), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)out,
@@ -1435,12 +1454,12 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
                        part_ml, G, Hpg, top_k, q_begin, seq_len);
   if constexpr (E::is_bf16) {
     if (top_k <= 16)
-      hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(256), 0, st,
+      hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(512), 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
                          shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
                          q_begin, q_count, seq_len);
     else
-      hipLaunchKernelGGL((qtile_attn_bf16_kernel<64>), dim3((unsigned)npairs), dim3(256), 0, st,
+      hipLaunchKernelGGL((qtile_attn_bf16_kernel<64>), dim3((unsigned)npairs), dim3(512), 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
                          shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
                          q_begin, q_count, seq_len);

@@ -307,7 +307,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_prefill_kernel(
   typedef PrefillLds<DI> C;
   constexpr int RT = 2;
   constexpr int kRows = 128 * RT;  // rows per workgroup
-  __shared__ __align__(16) uint8_t lds[2][C::kBufBytes];
+  __shared__ __align__(16) uint8_t lds0[C::kBufBytes];
+  __shared__ __align__(16) uint8_t lds1[C::kBufBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q = lane >> 5;
@@ -337,13 +338,15 @@ __global__ __launch_bounds__(256, 2) void index_topk_prefill_kernel(
       for (int s = 0; s < C::kSteps; ++s)
         qop[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u};
     }
-    prefill_issue_block<DI>(k_idx, 0, lds[0], wave, lane);
+    prefill_issue_block<DI>(k_idx, 0, lds0, wave, lane);
     MSA_WAIT_VMCNT(0);
     __syncthreads();
-    for (int c = 0; c < cmax; ++c) {
+    // unrolled by two so that every access names its buffer: the loads of block c + 1
+    // then provably do not alias the reads of block c
+    auto block = [&](int c, const uint8_t* cbuf, uint8_t* nbuf) {
       const bool has_next = c + 1 < cmax;
-      if (has_next) prefill_issue_block<DI>(k_idx, c + 1, lds[(c + 1) & 1], wave, lane);
-      const uint8_t* kb = lds[c & 1];
+      if (has_next) prefill_issue_block<DI>(k_idx, c + 1, nbuf, wave, lane);
+      const uint8_t* kb = cbuf;
       float mx[RT] = {-INFINITY, -INFINITY};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
@@ -380,6 +383,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_prefill_kernel(
       }
       if (has_next) MSA_WAIT_VMCNT(0);  // this wave's part of block c + 1 has landed
       __syncthreads();
+    };
+    for (int c = 0; c < cmax; c += 2) {
+      block(c, lds0, lds1);
+      if (c + 1 < cmax) block(c + 1, lds1, lds0);
     }
   }
   if (!own) return;
