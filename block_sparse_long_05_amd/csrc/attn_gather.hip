@@ -140,6 +140,14 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
     const int64_t key0 = (int64_t)c * kBlock + koff;
     const int nvalid = (int)min((int64_t)kspan, limit - key0);
     if (nvalid <= 0) continue;
+    // rows koff .. of block c: contiguous caches, or the block's page (decode)
+    const elem* kblk = kbase + key0 * kHeadDim;
+    const elem* vblk = vbase + key0 * kHeadDim;
+    if (decode && p.pages.table != nullptr) {
+      const int64_t in_page = ((int64_t)g * kBlock + koff) * kHeadDim;
+      kblk = p.pages.block((const elem*)p.k, kbase, bseq, c, (int64_t)kBlock * kHeadDim) + in_page;
+      vblk = p.pages.block((const elem*)p.v, vbase, bseq, c, (int64_t)kBlock * kHeadDim) + in_page;
+    }
 
     // Half-block (64-key) bf16 units issue their V rows together with the K rows, so
     // the wave pays one memory round trip for both.
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
     uint32_t vpre[kPreV ? 64 : 1];
     if constexpr (kPreV) {
       if (kspan == 64) {
-        const elem* vp0 = vbase + key0 * kHeadDim + 2 * lane;
+        const elem* vp0 = vblk + 2 * lane;
 #pragma unroll
         for (int j = 0; j < 64; ++j)
           vpre[j] = j < nvalid ? *reinterpret_cast<const uint32_t*>(vp0 + (int64_t)j * kHeadDim) : 0u;
@@ -162,7 +170,7 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
       if (kt < ntiles) {
         const int kk = 16 * kt + hcol;
         const bool ok = kk < nvalid;
-        const elem* kp = kbase + (key0 + (ok ? kk : 0)) * kHeadDim + kgrp * E::kPerLane;
+        const elem* kp = kblk + (ok ? kk : 0) * kHeadDim + kgrp * E::kPerLane;
 #pragma unroll
         for (int s = 0; s < kNStep; ++s) a = mfma16(ok ? O::load(kp + s * O::kStep) : O::zero(), qop[s], a);
       }
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
         }
       }
     } else {
-      const elem* vp = vbase + key0 * kHeadDim + 2 * lane;
+      const elem* vp = vblk + 2 * lane;
       // V rows in batches of 16 so that many loads are in flight per wave.
       for (int j0 = 0; j0 < nvalid; j0 += 16) {
         float2 vv[16];

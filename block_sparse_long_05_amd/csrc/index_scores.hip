@@ -434,7 +434,7 @@ template <class E, int DI>
 __global__ __launch_bounds__(256) void index_scores_decode_kernel(
     const typename E::elem* __restrict__ q_idx, const typename E::elem* __restrict__ k_idx,
     float* __restrict__ block_scores, const int32_t* __restrict__ seq_lens, int64_t max_len,
-    int G, int top_k, int nblk, int blocks_per_wg) {
+    int G, int top_k, int nblk, int blocks_per_wg, PageMap pm) {
   typedef typename E::elem elem;
   typedef typename Operand<E>::type op_t;
   constexpr int kStep = 4 * E::kPerLane;  // dims per 16x16 MFMA k-step
@@ -462,7 +462,8 @@ __global__ __launch_bounds__(256) void index_scores_decode_kernel(
         qop[s] = ok ? Operand<E>::load(qp + s * kStep) : Operand<E>::zero();
     }
     for (int c = c0 + wave; c < c1; c += 4) {
-      const elem* kp = kbase + ((int64_t)c * kBlock + (lane & 15)) * DI + (lane >> 4) * E::kPerLane;
+      const elem* kp = pm.block(k_idx, kbase, b, c, (int64_t)kBlock * DI) + (lane & 15) * DI +
+                       (lane >> 4) * E::kPerLane;
       // bf16: the whole block's operands (32 x 16 B per lane) are in flight before the
       // first MFMA; fp32 (a correctness configuration) loads one 16-key tile at a time.
       constexpr int kGroup = E::is_bf16 ? 8 : 1;
@@ -520,7 +521,7 @@ __device__ __forceinline__ void scan_issue_stage(const uint16_t* rows, uint8_t* 
 __global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     float* __restrict__ block_scores, const int32_t* __restrict__ seq_lens, int64_t max_len,
-    int G, int top_k, int nblk, int blocks_per_wg) {
+    int G, int top_k, int nblk, int blocks_per_wg, PageMap pm) {
   __shared__ __align__(16) uint8_t lds[4][kScanRing][kScanStage];  // 128 KiB
   constexpr int kPerBlock = kBlock / kScanKeys;                      // stages per block
   const int lane = threadIdx.x & 63;
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
   const int nstages = nb > 0 ? kPerBlock * nb : 0;
   auto stage_rows = [&](int st) {
     const int c = c0 + wave + 4 * (st / kPerBlock);
-    return kbase + ((int64_t)c * kBlock + (st % kPerBlock) * kScanKeys) * 128;
+    return pm.block(k_idx, kbase, b, c, (int64_t)kBlock * 128) + (st % kPerBlock) * kScanKeys * 128;
   };
   for (int st = 0; st < kScanRing - 1 && st < nstages; ++st)
     scan_issue_stage(stage_rows(st), lds[wave][st], lane);
@@ -634,7 +635,7 @@ hipError_t launch_index_scores_prefill(int bf16, int index_dim, const void* q_id
 template <class E, int DI>
 static hipError_t launch_decode_t(const void* q_idx, const void* k_idx, float* bs,
                                   const int32_t* seq_lens, int B, int64_t max_len, int G,
-                                  int top_k, int nblk, hipStream_t st) {
+                                  int top_k, int nblk, PageMap pm, hipStream_t st) {
   // Enough workgroups to cover the chip several times over at long contexts,
   // each sweeping a contiguous run of blocks (multiple of the 4 waves).
   const int64_t total = (int64_t)B * nblk;
@@ -646,32 +647,32 @@ static hipError_t launch_decode_t(const void* q_idx, const void* k_idx, float* b
     if (G <= 16) {
       hipLaunchKernelGGL(index_scores_decode_lds_kernel, dim3(gx, B), dim3(256), 0, st,
                          (const uint16_t*)q_idx, (const uint16_t*)k_idx, bs, seq_lens, max_len, G,
-                         top_k, nblk, (int)per);
+                         top_k, nblk, (int)per, pm);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((index_scores_decode_kernel<E, DI>), dim3(gx, B), dim3(256), 0, st,
                      (const typename E::elem*)q_idx, (const typename E::elem*)k_idx, bs, seq_lens,
-                     max_len, G, top_k, nblk, (int)per);
+                     max_len, G, top_k, nblk, (int)per, pm);
   return hipGetLastError();
 }
 
 hipError_t launch_index_scores_decode(int bf16, int index_dim, const void* q_idx,
                                       const void* k_idx, float* block_scores,
                                       const int32_t* seq_lens, int B, int64_t max_len, int G,
-                                      int top_k, int nblk, hipStream_t stream) {
+                                      int top_k, int nblk, PageMap pm, hipStream_t stream) {
   if (bf16) {
     if (index_dim == 128)
       return launch_decode_t<BF16, 128>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G,
-                                        top_k, nblk, stream);
+                                        top_k, nblk, pm, stream);
     return launch_decode_t<BF16, 64>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
-                                     nblk, stream);
+                                     nblk, pm, stream);
   }
   if (index_dim == 128)
     return launch_decode_t<F32, 128>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
-                                     nblk, stream);
+                                     nblk, pm, stream);
   return launch_decode_t<F32, 64>(q_idx, k_idx, block_scores, seq_lens, B, max_len, G, top_k,
-                                  nblk, stream);
+                                  nblk, pm, stream);
 }
 
 }  // namespace msa

@@ -83,7 +83,8 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q, const void* k,
                                 const void* v, const int32_t* block_idx, void* out,
-                                void* workspace, size_t workspace_bytes, hipStream_t st) {
+                                void* workspace, size_t workspace_bytes, hipStream_t st,
+                                PageMap pm = PageMap{}) {
   const size_t need = decode_ws_bytes(p, dense);
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
@@ -111,6 +112,7 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
   gp.nsplit = nsplit;
   gp.blocks_per_split = bps;
   gp.half_blocks = dense ? 0 : 1;
+  gp.pages = pm;
   hipError_t e = launch_gather_attn(gp, st);
   if (e != hipSuccess) return MSA_ERR_HIP;
   return hip_status(launch_decode_combine(gp.bf16, part_o, part_ml, out, p->batch, p->num_groups,
@@ -176,7 +178,8 @@ msa_status msa_index_scores(const msa_problem* p, const void* q_idx, const void*
   }
   return hip_status(launch_index_scores_decode(bf16, p->index_dim, q_idx, k_idx, block_scores,
                                                p->seq_lens, p->batch, p->max_len,
-                                               p->num_groups, p->top_k, nblk, as_stream(stream)));
+                                               p->num_groups, p->top_k, nblk, PageMap{},
+                                               as_stream(stream)));
 }
 
 msa_status msa_block_topk(const msa_problem* p, const float* block_scores, int32_t* block_idx,
@@ -260,6 +263,52 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
     return MSA_ERR_INVALID_ARGUMENT;
   return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
                               workspace_bytes, as_stream(stream));
+}
+
+namespace {
+// Host checks shared by the paged entry points.
+msa_status check_paged(const msa_problem* p, const int32_t* block_table, int32_t pages_per_seq,
+                       int64_t num_pages) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+  if (block_table == nullptr || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (pages_per_seq < 1 || num_pages < 1) return MSA_ERR_INVALID_ARGUMENT;
+  if (p->max_len != (int64_t)pages_per_seq * MSA_BLOCK_SIZE) return MSA_ERR_INVALID_ARGUMENT;
+  return MSA_OK;
+}
+}  // namespace
+
+msa_status msa_index_scores_paged(const msa_problem* p, const void* q_idx, const void* k_idx_pages,
+                                  const int32_t* block_table, int32_t pages_per_seq,
+                                  int64_t num_pages, float* block_scores, void* stream) {
+  msa_status st = check_paged(p, block_table, pages_per_seq, num_pages);
+  if (st != MSA_OK) return st;
+  if (!aligned16(q_idx) || !aligned16(k_idx_pages) || !aligned16(block_scores))
+    return MSA_ERR_INVALID_ARGUMENT;
+  const PageMap pm{block_table, pages_per_seq, num_pages,
+                   (int64_t)MSA_BLOCK_SIZE * p->index_dim};
+  return hip_status(launch_index_scores_decode(p->dtype == MSA_DTYPE_BF16, p->index_dim, q_idx,
+                                               k_idx_pages, block_scores, p->seq_lens, p->batch,
+                                               p->max_len, p->num_groups, p->top_k,
+                                               (int)nblk_of(p), pm, as_stream(stream)));
+}
+
+msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, const void* k_pages,
+                                        const void* v_pages, const int32_t* block_table,
+                                        int32_t pages_per_seq, int64_t num_pages,
+                                        const int32_t* block_idx, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  msa_status st = check_paged(p, block_table, pages_per_seq, num_pages);
+  if (st != MSA_OK) return st;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(block_idx) ||
+      !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  const PageMap pm{block_table, pages_per_seq, num_pages,
+                   (int64_t)p->num_groups * MSA_BLOCK_SIZE * MSA_HEAD_DIM};
+  return run_decode_attention(p, false, q, k_pages, v_pages, block_idx, out, workspace,
+                              workspace_bytes, as_stream(stream), pm);
 }
 
 msa_status msa_dense_gqa_attn(const msa_problem* p, const void* q, const void* k, const void* v,

@@ -13,10 +13,30 @@ hipError_t launch_index_scores_prefill(int bf16, int index_dim, const void* q_id
                                        int64_t q_count, int G, int top_k, int nblk,
                                        hipStream_t stream);
 
+// Paged caches: logical block c of sequence b lives in page table[b * pps + c] (a page
+// holds one 128-token block); table == nullptr means the contiguous per-sequence layout.
+// Page ids outside [0, num_pages) read page 0 instead (unspecified values, no fault).
+struct PageMap {
+  const int32_t* table;
+  int pps;            // pages per sequence (table row length)
+  int64_t num_pages;
+  int64_t page_elems; // elements per page of the tensor being addressed (per group for K/V)
+  // Start of block c of sequence b: `contig` is sequence b's base in the contiguous layout;
+  // `base` the paged tensor; `block_elems` the elements of one block in either layout.
+  template <class T>
+  __host__ __device__ const T* block(const T* base, const T* contig, int64_t b, int c,
+                                     int64_t block_elems) const {
+    if (table == nullptr) return contig + (int64_t)c * block_elems;
+    int64_t pg = table[b * pps + c];
+    if (pg < 0 || pg >= num_pages) pg = 0;
+    return base + pg * page_elems;
+  }
+};
+
 hipError_t launch_index_scores_decode(int bf16, int index_dim, const void* q_idx,
                                       const void* k_idx, float* block_scores,
                                       const int32_t* seq_lens, int B, int64_t max_len, int G,
-                                      int top_k, int nblk, hipStream_t stream);
+                                      int top_k, int nblk, PageMap pm, hipStream_t stream);
 
 // Fused prefill index scores + block max + top-k (bf16, top_k <= 16).
 hipError_t launch_index_topk_prefill(int index_dim, const void* q_idx, const void* k_idx,
@@ -48,6 +68,7 @@ struct GatherParams {
   int nsplit;            // decode: splits per (sequence, group)
   int blocks_per_split;  // decode
   int half_blocks;       // decode: each split covers one half (64 keys) of one listed block
+  PageMap pages;         // decode: paged K/V caches (pages.table == nullptr: contiguous)
 };
 
 hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);

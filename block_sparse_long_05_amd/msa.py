@@ -33,8 +33,8 @@ BLOCK = 128
 
 # Every symbol include/msa.h declares.
 EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
-            "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
-            "msa_status_string", "msa_abi_version"]
+            "msa_sparse_attn_decode", "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
+            "msa_dense_gqa_attn", "msa_workspace_size", "msa_status_string", "msa_abi_version"]
 
 
 class CProblem(ctypes.Structure):
@@ -74,11 +74,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.msa_index_scores_paged.argtypes = [pp, vp, vp, vp, i32, i64, vp, vp]
+    lib.msa_sparse_attn_decode_paged.argtypes = [pp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]
     lib.msa_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(sz)]
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
     lib.msa_abi_version.argtypes = []
     for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
+                 "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
                  "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
                  "msa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -176,6 +180,25 @@ def msa_block_topk(p: Problem, block_scores, block_idx, stream=None):
 def msa_index_topk(p: Problem, q_idx, k_idx, block_idx, stream=None):
     _check(load_library().msa_index_topk(ctypes.byref(p.c()), _ptr(q_idx), _ptr(k_idx),
                                          _ptr(block_idx), _stream(stream)), "msa_index_topk")
+
+
+def msa_index_scores_paged(p: Problem, q_idx, k_idx_pages, block_table, block_scores,
+                           stream=None):
+    """Decode index scan over a paged index-key cache (see include/msa.h)."""
+    _check(load_library().msa_index_scores_paged(
+        ctypes.byref(p.c()), _ptr(q_idx), _ptr(k_idx_pages), _ptr(block_table),
+        int(block_table.shape[1]), int(k_idx_pages.shape[0]), _ptr(block_scores),
+        _stream(stream)), "msa_index_scores_paged")
+
+
+def msa_sparse_attn_decode_paged(p: Problem, q, k_pages, v_pages, block_table, block_idx, out,
+                                 workspace=None, stream=None):
+    """Decode sparse attention reading each kept block from its page (see include/msa.h)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_sparse_attn_decode_paged(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+        int(block_table.shape[1]), int(k_pages.shape[0]), _ptr(block_idx), _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode_paged")
 
 
 def index_topk_supported(p: Problem) -> bool:

@@ -165,3 +165,29 @@ def decode_inputs(B: int, max_len: int, G: int, Hpg: int, D: int = 128, d_idx: i
     lens = torch.tensor(seq_lens, dtype=torch.int32, device=dev)
     return dict(q=q, k_cache=k_cache, v_cache=v_cache, q_idx=q_idx, k_idx=k_idx,
                 seq_lens=lens, planted=planted)
+
+
+def to_paged(x: dict, seed: int = 0, spare_pages: int = 3) -> dict:
+    """The decode caches of `x` (from decode_inputs) laid out in 128-token pages placed at
+    seeded random page ids, as a paged KV cache would hold them:
+        k_idx_pages [P, 128, d_idx]   k_pages, v_pages [P, G, 128, D]
+        block_table [B, max_len / 128] int32 (page of logical block c of sequence b)
+    P = B * max_len / 128 + spare_pages; the spare pages hold zeros. Only data moves."""
+    kc, vc, ki = x["k_cache"], x["v_cache"], x["k_idx"]
+    B, G, L, D = kc.shape
+    if L % BLOCK:
+        raise ValueError("max_len must be a multiple of 128 for a paged layout")
+    nb = L // BLOCK
+    d_idx = ki.shape[-1]
+    P = B * nb + spare_pages
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((int(seed) * 1_000_003 + 99991) & ((1 << 62) - 1))
+    perm = torch.randperm(P, generator=gen)[:B * nb].to(kc.device)
+    k_pages = torch.zeros((P, G, BLOCK, D), dtype=kc.dtype, device=kc.device)
+    v_pages = torch.zeros_like(k_pages)
+    k_idx_pages = torch.zeros((P, BLOCK, d_idx), dtype=ki.dtype, device=ki.device)
+    k_pages[perm] = kc.view(B, G, nb, BLOCK, D).permute(0, 2, 1, 3, 4).reshape(B * nb, G, BLOCK, D)
+    v_pages[perm] = vc.view(B, G, nb, BLOCK, D).permute(0, 2, 1, 3, 4).reshape(B * nb, G, BLOCK, D)
+    k_idx_pages[perm] = ki.view(B * nb, BLOCK, d_idx)
+    table = perm.view(B, nb).to(torch.int32).contiguous()
+    return dict(k_pages=k_pages, v_pages=v_pages, k_idx_pages=k_idx_pages, block_table=table)

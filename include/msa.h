@@ -159,6 +159,30 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged decode (the GQA KV cache as a server keeps it, reused as is: researchpapers.dev
+ * summary "Mechanism" and mlqm.cn blog section 3.1). The caches hold pages of 128 tokens,
+ * one selection block per page, in any order:
+ *   k_idx_pages [num_pages, 128, d]    k_pages, v_pages [num_pages, G, 128, D]
+ *   block_table int32 [B, pages_per_seq]: page of logical block c of sequence b
+ * with p->max_len == pages_per_seq * 128 (the per-sequence capacity); seq_lens as for
+ * decode. Table entries of blocks after a sequence's local block (L - 1) / 128 are not
+ * read. Page ids must lie in [0, num_pages); any other id reads page 0 (unspecified
+ * values, no fault). The results equal those of the contiguous calls on the same data:
+ * msa_index_scores_paged writes block_scores like msa_index_scores (decode), and
+ * msa_block_topk then works unchanged on logical block ids; msa_sparse_attn_decode_paged
+ * is msa_sparse_attn_decode reading each kept block from its page (same workspace size).
+ * mode must be MSA_MODE_DECODE (else MSA_ERR_INVALID_ARGUMENT).
+ */
+msa_status msa_index_scores_paged(const msa_problem* p, const void* q_idx, const void* k_idx_pages,
+                                  const int32_t* block_table, int32_t pages_per_seq,
+                                  int64_t num_pages, float* block_scores, void* stream);
+msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, const void* k_pages,
+                                        const void* v_pages, const int32_t* block_table,
+                                        int32_t pages_per_seq, int64_t num_pages,
+                                        const int32_t* block_idx, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * Dense GQA attention with the same heads (the baseline the researchpapers.dev summary
  * compares MSA against, "Key results"). Prefill: causal attention of query rows
  * [q_begin, q_begin + q_count) over keys j <= t. Decode: each sequence's query over

@@ -161,3 +161,29 @@ def test_index_topk_rejections():
     n = ctypes.c_size_t(7)
     assert lib.msa_workspace_size(ctypes.byref(ok.c()), msa.ENTRY["index_topk"],
                                   ctypes.byref(n)) == msa.MSA_OK and n.value == 0
+
+
+def test_paged_decode_validation():
+    """The paged entries check mode, table pointer, page counts and that max_len equals
+    pages_per_seq * 128 on the host, before any launch."""
+    lib = msa.load_library()
+    c = _decode(max_len=4096)   # 32 pages per sequence
+    bad_mode = _prefill().c()
+    ok_args = (FAKE, FAKE, FAKE, 32, 100, FAKE, 0)
+    assert lib.msa_index_scores_paged(ctypes.byref(bad_mode), *ok_args) == msa.MSA_ERR_INVALID_ARGUMENT
+    for args in ((FAKE, FAKE, 0, 32, 100, FAKE, 0),        # null table
+                 (FAKE, FAKE, FAKE + 2, 32, 100, FAKE, 0),  # misaligned table
+                 (FAKE, FAKE, FAKE, 31, 100, FAKE, 0),      # max_len != pages_per_seq * 128
+                 (FAKE, FAKE, FAKE, 0, 100, FAKE, 0),
+                 (FAKE, FAKE, FAKE, 32, 0, FAKE, 0),        # no pages
+                 (FAKE + 4, FAKE, FAKE, 32, 100, FAKE, 0)):  # misaligned q_idx
+        assert lib.msa_index_scores_paged(ctypes.byref(c), *args) == msa.MSA_ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
+                                  ctypes.byref(n)) == msa.MSA_OK
+    assert lib.msa_sparse_attn_decode_paged(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 31, 100,
+                                            FAKE, FAKE, FAKE, n.value, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT
+    assert lib.msa_sparse_attn_decode_paged(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 32, 100,
+                                            FAKE, FAKE, FAKE, n.value - 1, 0) \
+        == msa.MSA_ERR_WORKSPACE_TOO_SMALL

@@ -202,6 +202,47 @@ def test_decode_equals_last_prefill_row():
     assert np.max(np.abs(out_p[T - 1] - out_d[0])) <= 2e-2
 
 
+@pytest.mark.parametrize("B,L,G,Hpg,d_idx,top_k,dtype,lens", [
+    (3, 4096, 8, 8, 128, 16, "bf16", [4096, 1000, 129]),   # LDS scan, ragged lengths
+    (2, 2048, 20, 2, 64, 5, "f32", [2048, 777]),           # generic scan (G > 16, d = 64)
+    (2, 1024, 4, 4, 128, 3, "bf16", [1, 300]),              # L = 1, all blocks kept
+])
+def test_paged_decode_equals_contiguous(B, L, G, Hpg, d_idx, top_k, dtype, lens):
+    """The paged decode entries on pages scattered at random ids give bit-identical block
+    scores, block ids and outputs to the contiguous decode on the same data, and match the
+    oracle."""
+    x = synth.decode_inputs(B, L, G, Hpg, 128, d_idx, dtype=dtype, seed=B + L + G,
+                            planted_per_group=4, seq_lens=lens)
+    print(f"paged decode B={B} L={L} G={G} d_idx={d_idx} k={top_k} {dtype}", flush=True)
+    xd = _to(x)
+    pg = synth.to_paged(xd, seed=L)
+    p = msa.decode_problem(xd, top_k)
+    outs = []
+    for paged in (False, True):
+        bs = torch.full((B, G, p.nblk), -7.0, dtype=torch.float32, device="cuda")
+        idx = msa.alloc_block_idx(p)
+        out = torch.zeros_like(xd["q"])
+        ws = msa.alloc_workspace(p, "sparse_attn_decode")
+        if paged:
+            msa.msa_index_scores_paged(p, xd["q_idx"], pg["k_idx_pages"], pg["block_table"], bs)
+        else:
+            msa.msa_index_scores(p, xd["q_idx"], xd["k_idx"], bs)
+        msa.msa_block_topk(p, bs, idx)
+        if paged:
+            msa.msa_sparse_attn_decode_paged(p, xd["q"], pg["k_pages"], pg["v_pages"],
+                                             pg["block_table"], idx, out, ws)
+        else:
+            msa.msa_sparse_attn_decode(p, xd["q"], xd["k_cache"], xd["v_cache"], idx, out, ws)
+        torch.cuda.synchronize()
+        outs.append((bs, idx, out))
+    (bs1, idx1, out1), (bs2, idx2, out2) = outs
+    assert torch.equal(bs1, bs2) and torch.equal(idx1, idx2) and torch.equal(out1, out2)
+    res = orc.decode(x["q"], x["k_cache"], x["v_cache"], x["q_idx"], x["k_idx"], x["seq_lens"],
+                     top_k)
+    parity.check_decode(x, parity.np32(out2), idx2.cpu().numpy(), parity.np32(bs2), res, top_k,
+                        label="paged")
+
+
 def test_dense_decode_entry():
     B, L, G, Hpg = 3, 2500, 4, 8
     x = synth.decode_inputs(B, L, G, Hpg, 128, 128, dtype="bf16", seed=8, seq_lens=[2500, 700, 1])
