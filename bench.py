@@ -410,6 +410,23 @@ def run_decode(name, cfg, args, torch, msa, synth):
                       peak=PEAK_HBM_GBS, unit="GB/s", frac=scan_gbs / PEAK_HBM_GBS,
                       traffic=measured_traffic("index_scores_decode"), work_per_launch=scan_bytes, launch_ms=scan_ms),
     )
+    if args.paged:
+        # the same step on a paged copy of the caches (pages at seeded random ids)
+        pgd = synth.to_paged(x, seed=B)
+        pout = torch.empty_like(out)
+        pidx = torch.empty_like(idx)
+
+        def paged_step():
+            msa.msa_index_scores_paged(p, x["q_idx"], pgd["k_idx_pages"], pgd["block_table"], bs)
+            msa.msa_block_topk(p, bs, pidx)
+            msa.msa_sparse_attn_decode_paged(p, x["q"], pgd["k_pages"], pgd["v_pages"],
+                                             pgd["block_table"], pidx, pout, ws)
+        paged_ms = time_reps(torch, paged_step, args.steps)
+        res["paged"] = dict(us_per_step=paged_ms * 1e3, us_per_token=paged_ms * 1e3 / B,
+                            vs_contiguous=paged_ms / ms_plain,
+                            same_output=bool(torch.equal(pout, out) and torch.equal(pidx, idx)))
+        del pgd, pout, pidx
+        torch.cuda.empty_cache()
     if args.dense_reps > 0:
         dws = msa.alloc_workspace(p, "dense_gqa_attn")
         dout = torch.empty_like(out)  # `out` is checked against the oracle below
@@ -425,7 +442,9 @@ def run_decode(name, cfg, args, torch, msa, synth):
         f"kernels {res['kernel_us']}  path {res['path_gbs']:.0f} GB/s "
         f"({res['path_frac_of_hbm']*100:.1f}% of HBM)  scan {scan_gbs:.0f} GB/s"
         + (f"  dense {res['dense']['us_per_step']:.0f} us/step, MSA speedup "
-           f"{res['dense']['speedup']:.1f}x" if "dense" in res else ""))
+           f"{res['dense']['speedup']:.1f}x" if "dense" in res else "")
+        + (f"  paged {res['paged']['us_per_step']:.1f} us/step (same output: "
+           f"{res['paged']['same_output']})" if "paged" in res else ""))
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = decode_oracle_sample(name, cfg, x, out, idx, args,
                                                                   torch)
@@ -486,6 +505,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefill query rows per call (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged", type=int, default=1,
+                    help="also time the decode step on a paged copy of the caches (1/0)")
     ap.add_argument("--dense-reps", type=int, default=1,
                     help="timed runs of the dense GQA entry point on the same workload "
                          "(speedup context; 0 = skip)")

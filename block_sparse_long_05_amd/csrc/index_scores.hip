@@ -547,9 +547,21 @@ __global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
   // This wave's blocks c0 + wave, c0 + wave + 4, ...: stages (block, quarter) in order.
   const int nb = (c1 - (c0 + wave) + 3) / 4;
   const int nstages = nb > 0 ? kPerBlock * nb : 0;
+  // Paged caches: lane j holds the page of this wave's j-th block (at most 16 of them),
+  // read once here. Looking the page up next to each block's loads would make the wait
+  // for that lookup also wait for every stage already in flight.
+  int my_page = 0;
+  if (pm.table != nullptr && lane < nb) {
+    int64_t pg = pm.table[(int64_t)b * pm.pps + c0 + wave + 4 * lane];
+    my_page = (pg < 0 || pg >= pm.num_pages) ? 0 : (int)pg;
+  }
   auto stage_rows = [&](int st) {
-    const int c = c0 + wave + 4 * (st / kPerBlock);
-    return pm.block(k_idx, kbase, b, c, (int64_t)kBlock * 128) + (st % kPerBlock) * kScanKeys * 128;
+    const int j = st / kPerBlock;
+    const uint16_t* blk =
+        pm.table != nullptr
+            ? k_idx + (int64_t)__builtin_amdgcn_readlane(my_page, j) * pm.page_elems
+            : kbase + (int64_t)(c0 + wave + 4 * j) * (kBlock * 128);
+    return blk + (st % kPerBlock) * kScanKeys * 128;
   };
   for (int st = 0; st < kScanRing - 1 && st < nstages; ++st)
     scan_issue_stage(stage_rows(st), lds[wave][st], lane);
