@@ -167,6 +167,36 @@ def decode_inputs(B: int, max_len: int, G: int, Hpg: int, D: int = 128, d_idx: i
                 seq_lens=lens, planted=planted)
 
 
+def random_selection(q_count: int, G: int, top_k: int, q_begin: int = 0, seed: int = 0,
+                     popular_per_group: int = 0) -> torch.Tensor:
+    """A valid block selection drawn at random, int32 [q_count, G, top_k] on the CPU: row i
+    (token t = q_begin + i, local block b = t // 128) holds b and top_k - 1 distinct blocks
+    of [0, b) (every block 0..b when b + 1 <= top_k), ascending, padded with -1. Each group
+    has popular_per_group blocks that every row able to see them picks first, so blocks
+    are kept by long runs of rows as well as by single rows. No scores are involved."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((int(seed) * 7919 + 104729) & ((1 << 62) - 1))
+    t = q_begin + torch.arange(q_count)
+    b = t // BLOCK
+    nblk = int(b.max().item()) + 1 if q_count > 0 else 1
+    r = torch.rand((q_count, G, nblk), generator=gen)
+    if popular_per_group > 0:
+        for g in range(G):
+            pop = torch.randperm(nblk, generator=gen)[:popular_per_group]
+            r[:, g, pop] -= 2.0
+    c = torch.arange(nblk)
+    big = 1e9
+    r = torch.where(c[None, None, :] < b[:, None, None], r, torch.full_like(r, big))
+    r = torch.where(c[None, None, :] == b[:, None, None], torch.full_like(r, -big), r)
+    kk = min(top_k, nblk)
+    val, pick = torch.topk(r, kk, dim=2, largest=False)
+    pick = torch.where(val < big, pick, torch.full_like(pick, 1 << 30))
+    pick, _ = torch.sort(pick, dim=2)
+    out = torch.full((q_count, G, top_k), -1, dtype=torch.int32)
+    out[:, :, :kk] = torch.where(pick < (1 << 30), pick, torch.full_like(pick, -1)).to(torch.int32)
+    return out
+
+
 def to_paged(x: dict, seed: int = 0, spare_pages: int = 3) -> dict:
     """The decode caches of `x` (from decode_inputs) laid out in 128-token pages placed at
     seeded random page ids, as a paged KV cache would hold them:

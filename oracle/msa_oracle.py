@@ -253,6 +253,111 @@ def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
 
 
 # ----------------------------------------------------------------------------------
+# Index-branch KL loss (training side)
+#
+# researchpapers.dev summary, "Mechanism": the Index Branch is trained with a KL loss
+# towards the Main Branch's distribution on the selected blocks, and the gradient from
+# the index path into the main attention is cut. Readings (the pages give no formula):
+#   R12 the target P of a (query t, group g) row is the main branch's token-level
+#       attention distribution over the visible tokens of the selected blocks, averaged
+#       over the Hpg heads of the group (one index query serves the whole group);
+#   R13 the index distribution I is a softmax of index_scale * q_idx[t, g] . k_idx[j]
+#       over the same tokens (index_scale is the caller's temperature; selection is
+#       unaffected by it);
+#   R14 loss = KL(P || I) = sum_j P_j (ln P_j - ln I_j), with 0 ln 0 = 0;
+#   R15 P is a constant (stop-gradient): gradients flow only into q_idx and k_idx,
+#       and they are the gradients of the sum of the per-row losses;
+#   R16 a row with no visible selected token has loss 0 and zero gradient.
+# ----------------------------------------------------------------------------------
+
+def kl_row(q_t, k_g, q_idx_tg, k_idx, sel, t: int, index_scale: float,
+           block: int = BLOCK) -> dict:
+    """KL(P || I) of one (query, group) row and its gradient.
+
+    q_t [Hpg, D] the group's query heads at position t; k_g [T, D] the group's keys;
+    q_idx_tg [d]; k_idx [T, d]; sel the selected block ids (ids < 0 ignored).
+    Returns dict(loss, dq [d], keys (token ids), gx (d loss / d index score of each
+    token, already times index_scale), p_plus_i (P_j + I_j), and the magnitude sums the device
+    comparison uses: dq_abs = sum_j |gx_j| |k_idx[j]|, mass_abs = index_scale *
+    sum_j (P_j + I_j) |k_idx[j]|, loss_abs = sum_j P_j |ln P_j - ln I_j|)."""
+    q_t = as_f64(q_t)
+    qi = as_f64(q_idx_tg)
+    d = qi.shape[-1]
+    sel = [int(c) for c in np.asarray(sel).ravel().tolist() if int(c) >= 0]
+    keys = visible_keys(sel, t, block)
+    if len(keys) == 0:                           # R16
+        z = np.zeros(d)
+        return dict(loss=0.0, dq=z, keys=keys, gx=np.zeros(0), p_plus_i=np.zeros(0),
+                    dq_abs=z, mass_abs=z, loss_abs=0.0)
+    D = q_t.shape[-1]
+    kk = as_f64(k_g[keys])
+    ki = as_f64(k_idx[keys])
+    # main branch distribution per head (R9 scale), then the mean over the group (R12)
+    logits = (q_t @ kk.T) / math.sqrt(D)
+    logits = logits - logits.max(axis=1, keepdims=True)
+    ph = np.exp(logits)
+    ph = ph / ph.sum(axis=1, keepdims=True)
+    P = ph.mean(axis=0)
+    # index distribution (R13), kept in log form
+    x = index_scale * (ki @ qi)
+    xm = x.max()
+    log_i = x - (xm + math.log(np.exp(x - xm).sum()))
+    I = np.exp(log_i)
+    pos = P > 0.0                                # R14: 0 ln 0 = 0
+    diff = np.zeros_like(P)
+    diff[pos] = np.log(P[pos]) - log_i[pos]
+    loss = float((P * diff).sum())
+    gx = index_scale * (I - P)                   # d loss / d (q_idx . k_idx[j])
+    return dict(loss=loss, dq=gx @ ki, keys=keys, gx=gx, p_plus_i=P + I,
+                dq_abs=np.abs(gx) @ np.abs(ki),
+                mass_abs=index_scale * ((P + I) @ np.abs(ki)),
+                loss_abs=float((P * np.abs(diff)).sum()))
+
+
+def index_kl(q, k, q_idx, k_idx, block_idx, index_scale: float, q_begin: int = 0,
+             rows=None, block: int = BLOCK) -> dict:
+    """Index-branch KL loss and gradients for chunk rows `rows` (default: all).
+
+    q [T, G*Hpg, D]; k [G, T, D]; q_idx [T, G, d]; k_idx [T, d];
+    block_idx [R, G, top_k]: row i is token q_begin + i. Returns dict(loss [n, G],
+    dq_idx [n, G, d], dk_idx [T, d] (the sum over the given rows of each row's
+    gradient with respect to the index keys), dq_abs [n, G, d], mass_abs [n, G, d],
+    loss_abs [n, G], dk_abs [T, d] = sum |gx_j| |q_idx|, dk_mass [T, d] =
+    index_scale * sum (P_j + I_j) |q_idx|, rows)."""
+    q, k = host_small_f64(q), host_small_f64(k)
+    q_idx, k_idx = host_small_f64(q_idx), host_small_f64(k_idx)
+    bi = np.asarray(host(block_idx))
+    T, Hq, _ = q.shape
+    G = k.shape[0]
+    Hpg = Hq // G
+    d = q_idx.shape[-1]
+    rows = np.arange(bi.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = len(rows)
+    loss = np.zeros((n, G))
+    loss_abs = np.zeros((n, G))
+    dq = np.zeros((n, G, d))
+    dq_abs = np.zeros((n, G, d))
+    mass_abs = np.zeros((n, G, d))
+    dk = np.zeros((T, d))
+    dk_abs = np.zeros((T, d))
+    dk_mass = np.zeros((T, d))
+    for a, i in enumerate(rows.tolist()):
+        t = q_begin + i
+        for g in range(G):
+            qi = as_f64(q_idx[t, g])
+            r = kl_row(q[t, g * Hpg:(g + 1) * Hpg], k[g], qi, k_idx, bi[i, g], t, index_scale,
+                       block)
+            loss[a, g], dq[a, g] = r["loss"], r["dq"]
+            dq_abs[a, g], mass_abs[a, g], loss_abs[a, g] = r["dq_abs"], r["mass_abs"], r["loss_abs"]
+            if len(r["keys"]):
+                dk[r["keys"]] += np.outer(r["gx"], qi)
+                dk_abs[r["keys"]] += np.outer(np.abs(r["gx"]), np.abs(qi))
+                dk_mass[r["keys"]] += index_scale * np.outer(r["p_plus_i"], np.abs(qi))
+    return dict(loss=loss, dq_idx=dq, dk_idx=dk, dq_abs=dq_abs, mass_abs=mass_abs,
+                loss_abs=loss_abs, dk_abs=dk_abs, dk_mass=dk_mass, rows=rows)
+
+
+# ----------------------------------------------------------------------------------
 # Dense GQA attention (the comparison baseline of the researchpapers.dev summary,
 # "Key results": MSA against dense GQA with the same heads)
 # ----------------------------------------------------------------------------------
