@@ -42,6 +42,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import scipy.sparse
 
 BLOCK = 128
 NEAR_TIE_REL = 1e-5
@@ -338,9 +339,9 @@ def index_kl(q, k, q_idx, k_idx, block_idx, index_scale: float, q_begin: int = 0
     dq = np.zeros((n, G, d))
     dq_abs = np.zeros((n, G, d))
     mass_abs = np.zeros((n, G, d))
-    dk = np.zeros((T, d))
-    dk_abs = np.zeros((T, d))
-    dk_mass = np.zeros((T, d))
+    # dk_idx[j] = sum over rows of gx_row[j] q_idx_row: the rows' token gradients are
+    # collected as a sparse [rows, T] matrix W and dk_idx = W^T . Q_idx (one product).
+    w_rows, w_keys, w_val, w_pi, qi_rows = [], [], [], [], []
     for a, i in enumerate(rows.tolist()):
         t = q_begin + i
         for g in range(G):
@@ -349,10 +350,22 @@ def index_kl(q, k, q_idx, k_idx, block_idx, index_scale: float, q_begin: int = 0
                        block)
             loss[a, g], dq[a, g] = r["loss"], r["dq"]
             dq_abs[a, g], mass_abs[a, g], loss_abs[a, g] = r["dq_abs"], r["mass_abs"], r["loss_abs"]
-            if len(r["keys"]):
-                dk[r["keys"]] += np.outer(r["gx"], qi)
-                dk_abs[r["keys"]] += np.outer(np.abs(r["gx"]), np.abs(qi))
-                dk_mass[r["keys"]] += index_scale * np.outer(r["p_plus_i"], np.abs(qi))
+            w_rows.append(np.full(len(r["keys"]), len(qi_rows)))
+            w_keys.append(r["keys"])
+            w_val.append(r["gx"])
+            w_pi.append(r["p_plus_i"])
+            qi_rows.append(qi)
+    if qi_rows:
+        shape = (len(qi_rows), T)
+        ij = (np.concatenate(w_rows), np.concatenate(w_keys))
+        W = scipy.sparse.csr_matrix((np.concatenate(w_val), ij), shape=shape)
+        S = scipy.sparse.csr_matrix((np.concatenate(w_pi), ij), shape=shape)
+        QI = np.stack(qi_rows)
+        dk = np.asarray(W.T @ QI)
+        dk_abs = np.asarray(abs(W).T @ np.abs(QI))
+        dk_mass = index_scale * np.asarray(S.T @ np.abs(QI))
+    else:
+        dk = dk_abs = dk_mass = np.zeros((T, d))
     return dict(loss=loss, dq_idx=dq, dk_idx=dk, dq_abs=dq_abs, mass_abs=mass_abs,
                 loss_abs=loss_abs, dk_abs=dk_abs, dk_mass=dk_mass, rows=rows)
 
