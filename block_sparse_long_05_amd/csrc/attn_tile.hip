@@ -32,6 +32,7 @@
 
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "msa_tile.h"
 
 namespace msa {
 
@@ -68,7 +69,8 @@ __device__ __forceinline__ bool in_shared(const int32_t* slist, int top_k, int c
 }
 
 // Bucket (g * nblk + c) of a kept entry that goes through the reverse index, -1 for
-// padding, invisible ids and entries of a shared block of the entry's query tile.
+// padding, invisible ids and entries of a shared block of the entry's query tile (no
+// shared lists: every visible entry goes through).
 __device__ __forceinline__ int64_t entry_bucket(const int32_t* block_idx, int64_t id, int G,
                                                 int top_k, int64_t q_begin, int nblk,
                                                 const int32_t* shared, int QT) {
@@ -78,7 +80,7 @@ __device__ __forceinline__ int64_t entry_bucket(const int32_t* block_idx, int64_
   const int64_t i = rowg / G;
   const int64_t t = q_begin + i;
   if (c < 0 || (int64_t)c > t / kBlock) return -1;
-  if (in_shared(shared + ((i / QT) * G + g) * top_k, top_k, c)) return -1;
+  if (shared != nullptr && in_shared(shared + ((i / QT) * G + g) * top_k, top_k, c)) return -1;
   return (int64_t)g * nblk + c;
 }
 
@@ -126,7 +128,6 @@ __global__ __launch_bounds__(256) void kv_classify_kernel(const int32_t* __restr
 // token, in separate cache lines: count[stripe * nbuckets + bucket]. The scan walks
 // buckets in order and stripes within a bucket, so the sorted entries of one bucket
 // stay contiguous.
-constexpr int kStripes = 16;
 
 __global__ void kv_count_kernel(const int32_t* __restrict__ block_idx, int64_t n_entries, int G,
                                 int top_k, int64_t q_begin, int nblk, const int32_t* __restrict__ shared,
@@ -545,46 +546,6 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
 }
 
 
-// ---- bf16 K staging by direct global->LDS loads (row-swizzled, unpadded) -----------------
-// Row r of the staged block occupies 256 bytes; its 16-byte chunk x sits at position
-// x ^ (r % 16), so a quarter-wave loads one whole row (coalesced) and the S^T operand reads
-// of 8 rows at a time hit distinct banks.
-// V blocks use another row swizzle (kVSwz): chunk x of row r sits at position
-// x ^ (4 (r % 4) + (r / 4) % 4), which keeps the transpose reads of PV (4 rows x 4
-// chunks per half-wave) on 16 distinct positions.
-__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-template <int NT, bool kVSwz = false>
-__device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int64_t seq_len,
-                                            uint8_t* kbuf, int tid) {
-  const int64_t key0 = (int64_t)c * kBlock;
-  const int nk = (int)min((int64_t)kBlock, seq_len - key0);
-  const uint16_t* kg = K + ((int64_t)g * seq_len + key0) * kHeadDim;
-  const int wave = tid >> 6, lane = tid & 63;
-  constexpr int kLoads = kBlock * 256 / 1024;  // 1 KiB loads per block
-#pragma unroll
-  for (int i = 0; i < kLoads / (NT / 64); ++i) {
-    const int li = wave * (kLoads / (NT / 64)) + i;
-    const int r = 4 * li + (lane >> 4);
-    const int chunk = (lane & 15) ^ (kVSwz ? v_swz(r) : (r & 15));
-    const int rr = r < nk ? r : nk - 1;  // rows past the sequence end repeat a valid row
-    const uint32_t off = (uint32_t)(rr * kHeadDim + chunk * 8);  // 32-bit: uniform base + offset
-    __builtin_amdgcn_global_load_lds((const void*)(kg + off),
-                                     (__attribute__((address_space(3))) void*)(kbuf + li * 1024),
-                                     16, 0, 0);
-  }
-}
-
-__device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
-  f32x16 acc = {};
-#pragma unroll
-  for (int s = 0; s < kHeadDim / 16; ++s) {
-    const int pos = (2 * s + q) ^ (m & 15);
-    acc = mfma32(*reinterpret_cast<const u32x4*>(kbuf + m * 256 + pos * 16), qop[s], acc);
-  }
-  return acc;
-}
-
 // O^T += V^T . P^T over one 64-key half of the block (bf16): chunk u of the half holds keys
 // 64 * half + 16 u + {4q .. 4q+3, 8 + 4q .. 8 + 4q + 3}, the keys of its P^T registers.
 __device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const uint16_t* vt,
@@ -597,46 +558,6 @@ __device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const u
       const uint16_t* vr = vt + (32 * dt + m) * kVRow + 64 * half + 16 * u + 4 * q;
       const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
-    }
-  }
-}
-
-// O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the V
-// row swizzle of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
-// lane i of a 16-lane group column i % 4 of the 8-byte rows that lanes 4 j + i / 4
-// (j = 0..3) address. Lane (m = lane % 32, q = lane / 32) needs D column 32 dt + m of
-// keys 16 u + 4 q + 0..3 (then + 8): so lane r of its group addresses key row
-// 16 u + 4 q + r / 4, columns 32 dt + 16 ((lane / 16) % 2) + 4 (r % 4) .. + 4.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s*)(const_cast<uint8_t*>(p)));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-__device__ __forceinline__ void pv_half_tr(f32x16* o, const u32x4* pb, const uint8_t* vbuf,
-                                           int lane, int half) {
-  // Key row 16 u' + 4 q + j (+ 8 for the second read) holds chunk (4 dt + c0) at position
-  // 4 (dt ^ j) + (c0 ^ q) (+ 2, xor, for the second read), with c0 = 2 hx + (r % 4) / 2.
-  const int q = lane >> 5, hx = (lane >> 4) & 1, r = lane & 15;
-  const int j = r >> 2;
-  const int c0 = 2 * hx + ((r & 3) >> 1);
-  const uint8_t* base = vbuf + (4 * q + j) * 256 + (r & 1) * 8;
-  const uint8_t* lo_b[4];
-  const uint8_t* hi_b[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    lo_b[dt] = base + 64 * (dt ^ j) + 16 * (c0 ^ q);
-    hi_b[dt] = base + 8 * 256 + 64 * (dt ^ j) + 16 * (c0 ^ q ^ 2);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row0 = 64 * half + 16 * u;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const u32x2 lo = lds_read_tr16(lo_b[dt] + row0 * 256);
-      const u32x2 hi = lds_read_tr16(hi_b[dt] + row0 * 256);
       o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
     }
   }
@@ -1392,6 +1313,29 @@ hipError_t launch_dense_prefill_bf16(const void* q, const void* k, const void* v
 // ---- host side -------------------------------------------------------------------------------
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
+void launch_exclusive_scan(int32_t* a, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, st, n, a);
+}
+
+void launch_reverse_index(const int32_t* block_idx, int64_t n_entries, int G, int top_k,
+                          int64_t q_begin, int nblk, const int32_t* shared, int QT,
+                          int32_t* count, int32_t* cursor, int32_t* offset, int32_t* sorted,
+                          hipStream_t st) {
+  const int64_t nb = (int64_t)G * nblk;
+  const unsigned grid_e = (unsigned)std::min<int64_t>((n_entries + 255) / 256, 65536);
+  const int64_t ncnt = nb * kStripes;
+  hipLaunchKernelGGL(kv_zero_kernel, dim3((unsigned)std::min<int64_t>((ncnt + 255) / 256, 4096)),
+                     dim3(256), 0, st, count, ncnt);
+  hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
+                     top_k, q_begin, nblk, shared, QT, count);
+  const unsigned grid_b = (unsigned)std::min<int64_t>((nb + 255) / 256, 65536);
+  hipLaunchKernelGGL(kv_bucket_total_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset);
+  launch_exclusive_scan(offset, nb, st);
+  hipLaunchKernelGGL(kv_cursor_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset, cursor);
+  hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
+                     top_k, q_begin, nblk, shared, QT, cursor, sorted);
+}
+
 size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, int nblk) {
   const int64_t nb = (int64_t)G * nblk;
   const int64_t E = q_count * G * top_k;
@@ -1428,21 +1372,11 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
   w += al256((size_t)n_entries * Hpg * 2 * 4);
   elem* part_o = reinterpret_cast<elem*>(w);
 
-  const unsigned grid_e = (unsigned)std::min<int64_t>((n_entries + 255) / 256, 65536);
-  const int64_t ncnt = nb * kStripes;
-  hipLaunchKernelGGL(kv_zero_kernel, dim3((unsigned)std::min<int64_t>((ncnt + 255) / 256, 4096)),
-                     dim3(256), 0, st, count, ncnt);
   const int64_t npairs = ntiles * G;
   hipLaunchKernelGGL(kv_classify_kernel, dim3((unsigned)((npairs + 3) / 4)), dim3(256), 0, st,
                      block_idx, shared, G, top_k, q_begin, q_count, QT, npairs);
-  hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, shared, QT, count);
-  const unsigned grid_b = (unsigned)std::min<int64_t>((nb + 255) / 256, 65536);
-  hipLaunchKernelGGL(kv_bucket_total_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset);
-  hipLaunchKernelGGL(kv_scan_kernel, dim3(1), dim3(1024), 0, st, nb, offset);
-  hipLaunchKernelGGL(kv_cursor_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset, cursor);
-  hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, shared, QT, cursor, sorted);
+  launch_reverse_index(block_idx, n_entries, G, top_k, q_begin, nblk, shared, QT, count, cursor,
+                       offset, sorted, st);
   const unsigned tiles = (unsigned)((n_entries + kTile - 1) / kTile);
   if constexpr (E::is_bf16)
     hipLaunchKernelGGL(kv_attn_bf16_kernel, dim3(tiles), dim3(256), 0, st, (const uint16_t*)q,

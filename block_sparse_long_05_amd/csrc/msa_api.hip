@@ -77,6 +77,11 @@ size_t prefill_kv_ws_bytes(const msa_problem* p) {
                             p->heads_per_group, p->top_k, (int)nblk_of(p));
 }
 
+size_t kl_ws_bytes(const msa_problem* p) {
+  return kl_workspace_bytes(p->q_count, p->num_groups, p->heads_per_group, p->top_k,
+                            (int)nblk_of(p));
+}
+
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -156,6 +161,10 @@ msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes
       return MSA_OK;
     case MSA_ENTRY_DENSE_GQA_ATTN:
       if (p->mode == MSA_MODE_DECODE) *bytes = decode_ws_bytes(p, true);
+      return MSA_OK;
+    case MSA_ENTRY_INDEX_KL:
+      if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
+      *bytes = kl_ws_bytes(p);
       return MSA_OK;
     default:
       return MSA_ERR_INVALID_ARGUMENT;
@@ -250,6 +259,27 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   gp.q_count = p->q_count;
   gp.seq_len = p->seq_len;
   return hip_status(launch_gather_attn(gp, as_stream(stream)));
+}
+
+msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void* k,
+                                const void* q_idx, const void* k_idx, const int32_t* block_idx,
+                                float index_scale, float* loss, float* dq_idx, float* dk_idx,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_PREFILL || p->dtype != MSA_DTYPE_BF16 || p->index_dim != 128)
+    return MSA_ERR_UNSUPPORTED;
+  if (!(index_scale > 0.f) || !(index_scale < 3.0e38f)) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
+      !aligned16(block_idx) || !aligned16(loss) || !aligned16(dq_idx) || !aligned16(dk_idx))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (p->q_count == 0) return MSA_OK;
+  if (workspace_bytes < kl_ws_bytes(p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_index_kl_prefill(q, k, q_idx, k_idx, block_idx, index_scale, loss,
+                                            dq_idx, dk_idx, workspace, p->num_groups,
+                                            p->heads_per_group, p->top_k, p->q_begin, p->q_count,
+                                            p->seq_len, (int)nblk_of(p), as_stream(stream)));
 }
 
 msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,

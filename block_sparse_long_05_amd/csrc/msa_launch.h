@@ -85,6 +85,25 @@ hipError_t launch_dense_prefill_bf16(const void* q, const void* k, const void* v
                                      int Hpg, int64_t q_begin, int64_t q_count, int64_t seq_len,
                                      hipStream_t stream);
 
+// Reverse index (attn_tile.hip): counting sort of the visible kept entries (those not in
+// `shared`, when given) by bucket g * nblk + c; offset[nb] = number sorted. count and cursor
+// hold kStripes * nb counters each, offset nb + 1.
+constexpr int kStripes = 16;
+void launch_reverse_index(const int32_t* block_idx, int64_t n_entries, int G, int top_k,
+                          int64_t q_begin, int nblk, const int32_t* shared, int QT,
+                          int32_t* count, int32_t* cursor, int32_t* offset, int32_t* sorted,
+                          hipStream_t st);
+// In-place exclusive scan of a[0 .. n) with the total written to a[n] (one workgroup).
+void launch_exclusive_scan(int32_t* a, int64_t n, hipStream_t st);
+
+// Index-branch KL loss and gradients (index_kl.hip), bf16, D = d_idx = 128.
+size_t kl_workspace_bytes(int64_t q_count, int G, int Hpg, int top_k, int nblk);
+hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_idx,
+                                   const void* k_idx, const int32_t* block_idx, float index_scale,
+                                   float* loss, float* dq_idx, float* dk_idx, void* workspace,
+                                   int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
+                                   int64_t seq_len, int nblk, hipStream_t st);
+
 hipError_t launch_kv_prefill(int bf16, const void* q, const void* k, const void* v,
                              const int32_t* block_idx, void* out, void* workspace, int G, int Hpg,
                              int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,

@@ -1,0 +1,118 @@
+// LDS staging of 128-token K / V / index-key blocks and the MFMA operand reads on them
+// (gfx950, bf16, head dim 128), shared by the main-branch tile kernels and the index-branch
+// KL kernels.
+#pragma once
+
+#include "msa_device.h"
+
+namespace msa {
+
+// ---- bf16 K staging by direct global->LDS loads (row-swizzled, unpadded) -----------------
+// Row r of the staged block occupies 256 bytes; its 16-byte chunk x sits at position
+// x ^ (r % 16), so a quarter-wave loads one whole row (coalesced) and the S^T operand reads
+// of 8 rows at a time hit distinct banks.
+// V blocks use another row swizzle (kVSwz): chunk x of row r sits at position
+// x ^ (4 (r % 4) + (r / 4) % 4), which keeps the transpose reads of PV (4 rows x 4
+// chunks per half-wave) on 16 distinct positions.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <int NT, bool kVSwz = false>
+__device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int64_t seq_len,
+                                            uint8_t* kbuf, int tid) {
+  const int64_t key0 = (int64_t)c * kBlock;
+  const int nk = (int)min((int64_t)kBlock, seq_len - key0);
+  const uint16_t* kg = K + ((int64_t)g * seq_len + key0) * kHeadDim;
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int kLoads = kBlock * 256 / 1024;  // 1 KiB loads per block
+#pragma unroll
+  for (int i = 0; i < kLoads / (NT / 64); ++i) {
+    const int li = wave * (kLoads / (NT / 64)) + i;
+    const int r = 4 * li + (lane >> 4);
+    const int chunk = (lane & 15) ^ (kVSwz ? v_swz(r) : (r & 15));
+    const int rr = r < nk ? r : nk - 1;  // rows past the sequence end repeat a valid row
+    const uint32_t off = (uint32_t)(rr * kHeadDim + chunk * 8);  // 32-bit: uniform base + offset
+    __builtin_amdgcn_global_load_lds((const void*)(kg + off),
+                                     (__attribute__((address_space(3))) void*)(kbuf + li * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kHeadDim / 16; ++s) {
+    const int pos = (2 * s + q) ^ (m & 15);
+    acc = mfma32(*reinterpret_cast<const u32x4*>(kbuf + m * 256 + pos * 16), qop[s], acc);
+  }
+  return acc;
+}
+
+// O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the V
+// row swizzle of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
+// lane i of a 16-lane group column i % 4 of the 8-byte rows that lanes 4 j + i / 4
+// (j = 0..3) address. Lane (m = lane % 32, q = lane / 32) needs D column 32 dt + m of
+// keys 16 u + 4 q + 0..3 (then + 8): so lane r of its group addresses key row
+// 16 u + 4 q + r / 4, columns 32 dt + 16 ((lane / 16) % 2) + 4 (r % 4) .. + 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void pv_half_tr(f32x16* o, const u32x4* pb, const uint8_t* vbuf,
+                                           int lane, int half) {
+  // Key row 16 u' + 4 q + j (+ 8 for the second read) holds chunk (4 dt + c0) at position
+  // 4 (dt ^ j) + (c0 ^ q) (+ 2, xor, for the second read), with c0 = 2 hx + (r % 4) / 2.
+  const int q = lane >> 5, hx = (lane >> 4) & 1, r = lane & 15;
+  const int j = r >> 2;
+  const int c0 = 2 * hx + ((r & 3) >> 1);
+  const uint8_t* base = vbuf + (4 * q + j) * 256 + (r & 1) * 8;
+  const uint8_t* lo_b[4];
+  const uint8_t* hi_b[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    lo_b[dt] = base + 64 * (dt ^ j) + 16 * (c0 ^ q);
+    hi_b[dt] = base + 8 * 256 + 64 * (dt ^ j) + 16 * (c0 ^ q ^ 2);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row0 = 64 * half + 16 * u;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const u32x2 lo = lds_read_tr16(lo_b[dt] + row0 * 256);
+      const u32x2 hi = lds_read_tr16(hi_b[dt] + row0 * 256);
+      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
+    }
+  }
+}
+
+
+// One 32x32x16 MFMA operand read with the transpose read from a buffer of 256-byte rows in
+// the V swizzle: the 32 M (or N) indices are the buffer's columns 32 dt .. 32 dt + 31 (lane
+// l % 32 takes column 32 dt + l % 32) and the 16 K indices its rows row0 .. row0 + 15 (row0 a
+// multiple of 16), lane group q holding rows 4q + 0..3 and 8 + 4q + 0..3: the same order as
+// the keys of the P^T registers of an S^T tile, so either operand of a product over those
+// rows can be read this way.
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* buf, int row0, int dt, int lane) {
+  const int q = lane >> 5, hx = (lane >> 4) & 1, r = lane & 15;
+  const int j = r >> 2;
+  const int c0 = 2 * hx + ((r & 3) >> 1);
+  const uint8_t* base = buf + (row0 + 4 * q + j) * 256 + (r & 1) * 8;
+  const u32x2 lo = lds_read_tr16(base + 64 * (dt ^ j) + 16 * (c0 ^ q));
+  const u32x2 hi = lds_read_tr16(base + 8 * 256 + 64 * (dt ^ j) + 16 * (c0 ^ q ^ 2));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// S^T tile against a block staged in the V swizzle (row reads of 16-byte chunks).
+__device__ __forceinline__ f32x16 s_tile_vswz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < kHeadDim / 16; ++s) {
+    const int pos = (2 * s + q) ^ v_swz(m);
+    acc = mfma32(*reinterpret_cast<const u32x4*>(kbuf + m * 256 + pos * 16), qop[s], acc);
+  }
+  return acc;
+}
+
+}  // namespace msa

@@ -26,7 +26,7 @@ MSA_ERR_HIP = 4
 DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"prefill": 0, "decode": 1}
 ENTRY = {"index_scores": 0, "block_topk": 1, "sparse_attn_prefill": 2,
-         "sparse_attn_decode": 3, "dense_gqa_attn": 4, "index_topk": 5}
+         "sparse_attn_decode": 3, "dense_gqa_attn": 4, "index_topk": 5, "index_kl": 6}
 ALGO = {"auto": 0, "query_centric": 1, "kv_centric": 2}
 
 BLOCK = 128
@@ -34,7 +34,8 @@ BLOCK = 128
 # Every symbol include/msa.h declares.
 EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
-            "msa_dense_gqa_attn", "msa_workspace_size", "msa_status_string", "msa_abi_version"]
+            "msa_index_kl_prefill", "msa_dense_gqa_attn", "msa_workspace_size",
+            "msa_status_string", "msa_abi_version"]
 
 
 class CProblem(ctypes.Structure):
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.msa_index_scores_paged.argtypes = [pp, vp, vp, vp, i32, i64, vp, vp]
     lib.msa_sparse_attn_decode_paged.argtypes = [pp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]
+    lib.msa_index_kl_prefill.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                         sz, vp]
     lib.msa_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(sz)]
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
@@ -84,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
                  "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
                  "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
+                 "msa_index_kl_prefill",
                  "msa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -221,6 +225,17 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, block_idx, out, work
         _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode")
 
 
+def msa_index_kl_prefill(p: Problem, q, k, q_idx, k_idx, block_idx, index_scale: float, loss,
+                         dq_idx, dk_idx, workspace=None, stream=None):
+    """Index-branch KL loss (loss [q_count, G], dq_idx [q_count, G, 128] written) and its
+    index-key gradient (ADDED into dk_idx [T, 128]); all three fp32."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_index_kl_prefill(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
+        float(index_scale), _ptr(loss), _ptr(dq_idx), _ptr(dk_idx), _ptr(workspace), ws_bytes,
+        _stream(stream)), "msa_index_kl_prefill")
+
+
 def msa_dense_gqa_attn(p: Problem, q, k, v, out, workspace=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().msa_dense_gqa_attn(
@@ -280,6 +295,31 @@ def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None
         msa_block_topk(p, block_scores, block_idx, stream)
     msa_sparse_attn_prefill(p, q, x["k"], x["v"], block_idx, out, workspace, stream)
     return out, block_idx, block_scores
+
+
+def index_kl(x: dict, block_idx, top_k: int, index_scale: float, q_begin: int = 0,
+             q_count: Optional[int] = None, dk_idx=None, workspace=None, stream=None):
+    """Index-branch KL loss and gradients for query rows [q_begin, q_begin + q_count) on the
+    selection block_idx [q_count, G, top_k]. x holds q, k, q_idx, k_idx (bf16) on the device.
+    dk_idx (fp32 [T, 128]) is accumulated into; a zeroed one is made when it is None.
+    Returns (loss [q_count, G], dq_idx [q_count, G, 128], dk_idx)."""
+    q = x["q"]
+    T, Hq, D = q.shape
+    G = x["k"].shape[0]
+    if q_count is None:
+        q_count = T - q_begin
+    p = Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="prefill",
+                num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
+                top_k=top_k, head_dim=D, seq_len=T, q_begin=q_begin, q_count=q_count)
+    loss = torch.empty((q_count, G), dtype=torch.float32, device=q.device)
+    dq = torch.empty((q_count, G, x["q_idx"].shape[-1]), dtype=torch.float32, device=q.device)
+    if dk_idx is None:
+        dk_idx = torch.zeros((T, x["k_idx"].shape[-1]), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(p, "index_kl", q.device)
+    msa_index_kl_prefill(p, q, x["k"], x["q_idx"], x["k_idx"], block_idx, index_scale, loss, dq,
+                         dk_idx, workspace, stream)
+    return loss, dq, dk_idx
 
 
 def decode_problem(x: dict, top_k: int) -> Problem:

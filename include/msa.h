@@ -68,7 +68,8 @@ typedef enum {
   MSA_ENTRY_SPARSE_ATTN_PREFILL = 2,
   MSA_ENTRY_SPARSE_ATTN_DECODE = 3,
   MSA_ENTRY_DENSE_GQA_ATTN = 4,
-  MSA_ENTRY_INDEX_TOPK = 5
+  MSA_ENTRY_INDEX_TOPK = 5,
+  MSA_ENTRY_INDEX_KL = 6
 } msa_entry;
 
 /* Prefill main-branch algorithm. Both give the same result up to fp32 rounding. */
@@ -181,6 +182,35 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, con
                                         int32_t pages_per_seq, int64_t num_pages,
                                         const int32_t* block_idx, void* out, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Index-branch KL loss and its gradient, prefill (the training side of the index branch:
+ * researchpapers.dev summary, "Mechanism": the index branch learns the main branch's
+ * distribution on the selected blocks through a KL loss, and no gradient flows from it into
+ * the main attention). For chunk row i (token t = q_begin + i) and group g, over the tokens
+ * j <= t of the blocks listed in block_idx[i, g, :] (ids < 0 are padding, ids above the
+ * local block are ignored, listed ids must be distinct):
+ *   P_j = (1 / Hpg) sum over the group's heads h of softmax_j(q[t, h] . k[g, j] / sqrt(D))
+ *   I_j = softmax_j(index_scale * q_idx[t, g] . k_idx[j])
+ *   loss[i, g] = sum_j P_j (ln P_j - ln I_j)                        (0 ln 0 = 0)
+ *   dq_idx[i, g, :] = sum_j index_scale (I_j - P_j) k_idx[j]
+ *   dk_idx[j, :] += sum over the chunk's rows of index_scale (I_j - P_j) q_idx[t, g]
+ * P is a constant: these are the gradients of sum(loss) with respect to q_idx and k_idx
+ * only. A row with no visible kept token gets loss 0 and a zero gradient.
+ * Layouts: q [T, G*Hpg, 128], k [G, T, 128], q_idx [T, G, 128], k_idx [T, 128] (bf16, full
+ * tensors as for msa_sparse_attn_prefill); block_idx int32 [q_count, G, top_k]; loss fp32
+ * [q_count, G] and dq_idx fp32 [q_count, G, 128] are written; dk_idx fp32 [T, 128] is
+ * ADDED to (the caller zeroes it once, so the chunks of one sequence accumulate).
+ * Built for dtype bf16, index_dim 128 and mode prefill (else MSA_ERR_UNSUPPORTED);
+ * index_scale must be finite and > 0 (else MSA_ERR_INVALID_ARGUMENT). Loss and dq_idx are
+ * bit-identical from run to run; dk_idx sums each block's entries in the order the
+ * reverse index places them, which may vary from run to run at the level of fp32 rounding.
+ * Workspace: msa_workspace_size(p, MSA_ENTRY_INDEX_KL).
+ */
+msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void* k,
+                                const void* q_idx, const void* k_idx, const int32_t* block_idx,
+                                float index_scale, float* loss, float* dq_idx, float* dk_idx,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Dense GQA attention with the same heads (the baseline the researchpapers.dev summary

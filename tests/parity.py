@@ -87,3 +87,41 @@ def check_decode(x, out_gpu, idx_gpu, bs_gpu, res, top_k, label=""):
     err = float(np.max(np.abs(got - ref)))
     assert err <= tol, f"{label}: max abs err {err} > {tol}"
     return dict(err=err, near_ties=int(res["near_tie"].sum()), differ=len(differ))
+
+
+# ---- index-branch KL loss ---------------------------------------------------------------
+# The device keeps P and I in fp32 (errors ~1e-5 relative, from fp32 accumulation of the
+# logits and the exponentials) and rounds W = index_scale (I - P) to bf16 for the two
+# gradient products (relative error <= 2^-9 per term). Hence, per element:
+#   loss:   |err| <= KL_LOSS_REL * (1 + sum_j P_j |ln P_j - ln I_j|)
+#   dq, dk: |err| <= 2^-8 * sum_j |W_j| |x_j| + KL_MASS_REL * index_scale sum_j (P_j + I_j) |x_j|
+# (x the other operand: k_idx rows for dq, q_idx rows for dk), each bound ~10x above the
+# errors the arithmetic can make.
+KL_LOSS_REL = 2e-4
+KL_W_REL = 2.0 ** -8
+KL_MASS_REL = 1e-4
+
+
+def check_kl(loss, dq, ref, rows_gpu, dk=None, label=""):
+    """loss [n, G], dq [n, G, d] of the device rows rows_gpu vs the oracle dict `ref` of the
+    same rows; dk (the whole [T, d] gradient) vs ref["dk_idx"] when given."""
+    got_l = loss[rows_gpu].astype(np.float64)
+    tol_l = KL_LOSS_REL * (1.0 + ref["loss_abs"])
+    err_l = np.abs(got_l - ref["loss"])
+    assert (err_l <= tol_l).all(), (
+        f"{label} loss: {int((err_l > tol_l).sum())} rows off, worst {float(err_l.max())}")
+    got_q = dq[rows_gpu].astype(np.float64)
+    tol_q = KL_W_REL * ref["dq_abs"] + KL_MASS_REL * ref["mass_abs"] + 1e-7
+    err_q = np.abs(got_q - ref["dq_idx"])
+    assert (err_q <= tol_q).all(), (
+        f"{label} dq_idx: {int((err_q > tol_q).sum())} values off, worst ratio "
+        f"{float((err_q / tol_q).max())}")
+    out = dict(loss_max_err=float(err_l.max()), dq_worst_ratio=float((err_q / tol_q).max()))
+    if dk is not None:
+        tol_k = KL_W_REL * ref["dk_abs"] + KL_MASS_REL * ref["dk_mass"] + 1e-7
+        err_k = np.abs(dk.astype(np.float64) - ref["dk_idx"])
+        assert (err_k <= tol_k).all(), (
+            f"{label} dk_idx: {int((err_k > tol_k).sum())} values off, worst ratio "
+            f"{float((err_k / tol_k).max())}")
+        out["dk_worst_ratio"] = float((err_k / tol_k).max())
+    return out

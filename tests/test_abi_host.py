@@ -187,3 +187,31 @@ def test_paged_decode_validation():
     assert lib.msa_sparse_attn_decode_paged(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 32, 100,
                                             FAKE, FAKE, FAKE, n.value - 1, 0) \
         == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_index_kl_validation():
+    """The KL entry is built for bf16 prefill with index_dim 128; it checks the temperature,
+    pointer alignment and workspace size on the host, before any launch."""
+    lib = msa.load_library()
+    ok = _prefill()
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(ok.c()), msa.ENTRY["index_kl"],
+                                  ctypes.byref(n)) == msa.MSA_OK and n.value > 0
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def call(p, scale=0.1, ws=n.value, loss=FAKE):
+        return lib.msa_index_kl_prefill(ctypes.byref(p.c()), *args, ctypes.c_float(scale), loss,
+                                        FAKE, FAKE, FAKE, ws, 0)
+
+    for p in (_prefill(dtype="f32"), _prefill(index_dim=64)):
+        assert call(p) == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_kl_prefill(ctypes.byref(_decode()), *args, ctypes.c_float(0.1), FAKE,
+                                    FAKE, FAKE, FAKE, n.value, 0) == msa.MSA_ERR_UNSUPPORTED
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(ok, scale) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(ok, loss=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(ok, ws=n.value - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
+    assert call(_prefill(q_begin=4096, q_count=0), ws=0) == msa.MSA_OK
+    m = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(_decode()), msa.ENTRY["index_kl"],
+                                  ctypes.byref(m)) == msa.MSA_ERR_INVALID_ARGUMENT
