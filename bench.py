@@ -71,6 +71,23 @@ def prefill_attn_flops(T, Hq, D, top_k):
     return 4.0 * D * Hq * tot
 
 
+def kl_pairs(T, top_k):
+    """Visible kept (row, key) pairs per group of a causal prefill with full selections."""
+    tot = 0
+    for t_block in range((T + BLOCK - 1) // BLOCK):
+        n_in = min(BLOCK, T - t_block * BLOCK)
+        kept = min(top_k, t_block + 1) - 1
+        tot += n_in * BLOCK * kept + n_in * (n_in + 1) // 2
+    return tot
+
+
+def kl_flops(T, G, Hpg, D, d_idx, top_k):
+    """Index-branch KL loss + gradients: per visible kept pair, the main logits of the
+    group's heads (2 Hpg D), the index logit (2 d), and its share of dq_idx and dk_idx
+    (2 d each). The second pass's recomputation of the logits is not counted."""
+    return float(G * kl_pairs(T, top_k)) * (2.0 * Hpg * D + 6.0 * d_idx)
+
+
 def dense_prefill_flops(T, Hq, D):
     """Causal dense attention: 4 D FLOPs per (head, query t, visible key j <= t)."""
     return 4.0 * D * Hq * T * (T + 1) / 2
@@ -275,6 +292,9 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
         f"path {total_tflops:.1f} TFLOP/s ({res['path_frac_of_peak']*100:.1f}% of peak)  "
         f"index {idx_tflops:.1f} TFLOP/s")
+    if args.kl and cfg["dtype"] == "bf16" and d_idx == 128:
+        res["kl"] = run_kl(name, cfg, args, torch, msa, x, idx_full, chunks, T, G, Hpg, d_idx,
+                           top_k, peak)
     if args.dense_reps > 0:
         # dense causal GQA attention over the same rows (the speedup context): same chunks
         dout = torch.empty_like(q)  # its own output: `out` is checked against the oracle below
@@ -341,6 +361,45 @@ def prefill_oracle_sample(name, cfg, x, out, idx_full, args):
                near_tie_selection_differences=differ, ok=True)
     log(f"[{name}] oracle {base['value']:.3g} tok/s on {cores} threads; parity {par}")
     return base, par
+
+
+def run_kl(name, cfg, args, torch, msa, x, idx_full, chunks, T, G, Hpg, d_idx, top_k, peak):
+    """The index-branch KL loss and gradients over the selection the index branch just
+    made (training side; not part of the prefill step above)."""
+    scale = 1.0 / d_idx ** 0.5
+    kprobs = [msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                          index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n)
+              for c0, n in chunks]
+    kws = torch.empty(max(msa.msa_workspace_size(p, "index_kl") for p in kprobs),
+                      dtype=torch.uint8, device="cuda")
+    loss = torch.empty((T, G), dtype=torch.float32, device="cuda")
+    dq = torch.empty((T, G, d_idx), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((T, d_idx), dtype=torch.float32, device="cuda")
+
+    def kl_step():
+        dk.zero_()
+        for p, (c0, n) in zip(kprobs, chunks):
+            msa.msa_index_kl_prefill(p, x["q"], x["k"], x["q_idx"], x["k_idx"],
+                                     idx_full[c0:c0 + n], scale, loss[c0:c0 + n], dq[c0:c0 + n],
+                                     dk, kws)
+    kl_ms = time_reps(torch, kl_step, max(1, args.steps // 2))
+    fl = kl_flops(T, G, Hpg, 128, d_idx, top_k)
+    tf = fl / (kl_ms * 1e-3) / 1e12
+    # identities of the gradients at full size (fp64 on the device): each row's score
+    # gradients sum to zero, and sum_j dk[j] . k_idx[j] = sum_(t,g) dq[t,g] . q_idx[t,g]
+    dk64 = dk.double()
+    lhs = float((dk64 * x["k_idx"].double()).sum())
+    rhs = float((dq.double() * x["q_idx"].double()).sum())
+    zero_rel = float(dk64.sum(0).abs().max() / dk64.abs().sum(0).max())
+    out = dict(ms=kl_ms, tflops=tf, frac_of_peak=tf / peak, flops=fl, index_scale=scale,
+               loss_mean=float(loss.double().mean()), dk_sum_rel=zero_rel,
+               identity_rel=abs(lhs - rhs) / max(abs(lhs), abs(rhs), 1e-30))
+    log(f"[{name}] index KL loss+grad {kl_ms:.2f} ms ({tf:.0f} TFLOP/s, "
+        f"{tf / peak * 100:.1f}% of peak)  mean loss {out['loss_mean']:.4f}  "
+        f"sum dk rel {zero_rel:.2e}  identity rel {out['identity_rel']:.2e}")
+    del kws, loss, dq, dk
+    torch.cuda.empty_cache()
+    return out
 
 
 # ---- decode ------------------------------------------------------------------------------
@@ -505,6 +564,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefill query rows per call (0 = the workload's default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kl", type=int, default=1,
+                    help="also time the index-branch KL loss + gradients on the prefill's "
+                         "selection (1/0)")
     ap.add_argument("--paged", type=int, default=1,
                     help="also time the decode step on a paged copy of the caches (1/0)")
     ap.add_argument("--dense-reps", type=int, default=1,

@@ -90,16 +90,19 @@ def check_decode(x, out_gpu, idx_gpu, bs_gpu, res, top_k, label=""):
 
 
 # ---- index-branch KL loss ---------------------------------------------------------------
-# The device keeps P and I in fp32 (errors ~1e-5 relative, from fp32 accumulation of the
-# logits and the exponentials) and rounds W = index_scale (I - P) to bf16 for the two
-# gradient products (relative error <= 2^-9 per term). Hence, per element:
-#   loss:   |err| <= KL_LOSS_REL * (1 + sum_j P_j |ln P_j - ln I_j|)
-#   dq, dk: |err| <= 2^-8 * sum_j |W_j| |x_j| + KL_MASS_REL * index_scale sum_j (P_j + I_j) |x_j|
-# (x the other operand: k_idx rows for dq, q_idx rows for dk), each bound ~10x above the
-# errors the arithmetic can make.
-KL_LOSS_REL = 2e-4
-KL_W_REL = 2.0 ** -8
-KL_MASS_REL = 1e-4
+# The device keeps P and I in fp32 (relative errors ~1e-6: fp32 accumulation of exact bf16
+# products, the hardware exp2) and rounds W = index_scale (I - P) to bf16 for the two
+# gradient products. bf16 holds 8 significant bits, so that rounding moves each term by at
+# most 2^-8 of itself, and |err| <= 2^-8 sum_j |W_j| |x_j| is the worst case (x the other
+# operand: k_idx rows for dq, q_idx rows for dk); measured errors reach 0.6-0.8 of it, and
+# match a bf16-W emulation of the oracle to ~1e-8. Per element:
+#   loss:   |err| <= KL_LOSS_REL * (1 + sum_j P_j |ln P_j - ln I_j|)     (measured < 1e-6)
+#   dq, dk: |err| <= 2 * 2^-8 * sum_j |W_j| |x_j|
+#                    + KL_MASS_REL * index_scale * sum_j (P_j + I_j) |x_j|
+# the last term covering the fp32 errors of P and I where W cancels (I ~ P).
+KL_LOSS_REL = 2e-5
+KL_W_REL = 2.0 ** -7
+KL_MASS_REL = 1e-5
 
 
 def check_kl(loss, dq, ref, rows_gpu, dk=None, label=""):
