@@ -259,16 +259,16 @@ def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
 # researchpapers.dev summary, "Mechanism": the Index Branch is trained with a KL loss
 # towards the Main Branch's distribution on the selected blocks, and the gradient from
 # the index path into the main attention is cut. Readings (the pages give no formula):
-#   R12 the target P of a (query t, group g) row is the main branch's token-level
-#       attention distribution over the visible tokens of the selected blocks, averaged
-#       over the Hpg heads of the group (one index query serves the whole group);
-#   R13 the index distribution I is a softmax of index_scale * q_idx[t, g] . k_idx[j]
-#       over the same tokens (index_scale is the caller's temperature; selection is
-#       unaffected by it);
-#   R14 loss = KL(P || I) = sum_j P_j (ln P_j - ln I_j), with 0 ln 0 = 0;
-#   R15 P is a constant (stop-gradient): gradients flow only into q_idx and k_idx,
-#       and they are the gradients of the sum of the per-row losses;
-#   R16 a row with no visible selected token has loss 0 and zero gradient.
+#   K1 the target P of a (query t, group g) row is the main branch's token-level
+#      attention distribution over the visible tokens of the selected blocks, averaged
+#      over the Hpg heads of the group (one index query serves the whole group);
+#   K2 the index distribution I is a softmax of index_scale * q_idx[t, g] . k_idx[j]
+#      over the same tokens (index_scale is the caller's temperature; selection is
+#      unaffected by it);
+#   K3 loss = KL(P || I) = sum_j P_j (ln P_j - ln I_j), with 0 ln 0 = 0;
+#   K4 P is a constant (stop-gradient): gradients flow only into q_idx and k_idx,
+#      and they are the gradients of the sum of the per-row losses;
+#   K5 a row with no visible selected token has loss 0 and zero gradient.
 # ----------------------------------------------------------------------------------
 
 def kl_row(q_t, k_g, q_idx_tg, k_idx, sel, t: int, index_scale: float,
@@ -286,25 +286,25 @@ def kl_row(q_t, k_g, q_idx_tg, k_idx, sel, t: int, index_scale: float,
     d = qi.shape[-1]
     sel = [int(c) for c in np.asarray(sel).ravel().tolist() if int(c) >= 0]
     keys = visible_keys(sel, t, block)
-    if len(keys) == 0:                           # R16
+    if len(keys) == 0:                           # K5
         z = np.zeros(d)
         return dict(loss=0.0, dq=z, keys=keys, gx=np.zeros(0), p_plus_i=np.zeros(0),
                     dq_abs=z, mass_abs=z, loss_abs=0.0)
     D = q_t.shape[-1]
     kk = as_f64(k_g[keys])
     ki = as_f64(k_idx[keys])
-    # main branch distribution per head (R9 scale), then the mean over the group (R12)
+    # main branch distribution per head (R9 scale), then the mean over the group (K1)
     logits = (q_t @ kk.T) / math.sqrt(D)
     logits = logits - logits.max(axis=1, keepdims=True)
     ph = np.exp(logits)
     ph = ph / ph.sum(axis=1, keepdims=True)
     P = ph.mean(axis=0)
-    # index distribution (R13), kept in log form
+    # index distribution (K2), kept in log form
     x = index_scale * (ki @ qi)
     xm = x.max()
     log_i = x - (xm + math.log(np.exp(x - xm).sum()))
     I = np.exp(log_i)
-    pos = P > 0.0                                # R14: 0 ln 0 = 0
+    pos = P > 0.0                                # K3: 0 ln 0 = 0
     diff = np.zeros_like(P)
     diff[pos] = np.log(P[pos]) - log_i[pos]
     loss = float((P * diff).sum())
