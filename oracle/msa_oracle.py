@@ -149,6 +149,13 @@ def attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray,
     return (p @ values) / p.sum(axis=1, keepdims=True)
 
 
+def attend_lse(q_heads: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """Natural-log normaliser of each head's softmax: ln sum_j exp(q . k_j * scale), [H]."""
+    logits = (q_heads @ keys.T) * scale
+    m = logits.max(axis=1)
+    return m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+
+
 def visible_keys(sel, t: int, block: int = BLOCK) -> np.ndarray:
     """Token ids of the selected blocks that query position t can see (j <= t)."""
     parts = [np.arange(c * block, min(c * block + block, t + 1)) for c in sel]
@@ -167,14 +174,16 @@ def _row(q_t, k_g, v_g, q_idx_tg, k_idx, t, top_k, block, scale, bs=None):
                                     block)[0]
         sel, tie = select_blocks(bs, b, top_k)
     j = visible_keys(sel, t, block)
-    return attend(as_f64(q_t), as_f64(k_g[j]), as_f64(v_g[j]), scale), sel, tie, bs
+    qh, kk = as_f64(q_t), as_f64(k_g[j])
+    return attend(qh, kk, as_f64(v_g[j]), scale), sel, tie, bs, attend_lse(qh, kk, scale)
 
 
 def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) -> dict:
     """Causal MSA prefill for the query positions `rows` (default: all).
 
     q [T, G*Hpg, D]; k, v [G, T, D]; q_idx [T, G, d_idx]; k_idx [T, d_idx].
-    Returns dict(out [R, Hq, D], sel [R][G] -> ascending ids, near_tie [R, G] bool,
+    Returns dict(out [R, Hq, D], lse [R, Hq] (ln of each head's softmax normaliser),
+    sel [R][G] -> ascending ids, near_tie [R, G] bool,
     block_scores {(i, g): array of b scores} for rows that were scored, rows [R]).
     Inputs are widened to float64 slice by slice, as each row needs them.
     """
@@ -186,6 +195,7 @@ def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) ->
     scale = 1.0 / math.sqrt(D)                   # R9
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((len(rows), Hq, D))
+    lse = np.zeros((len(rows), Hq))
     sel_all = [[None] * G for _ in rows]
     tie = np.zeros((len(rows), G), dtype=bool)
     scores = {}
@@ -205,14 +215,15 @@ def prefill(q, k, v, q_idx, k_idx, top_k: int, block: int = BLOCK, rows=None) ->
             for g in range(G):
                 hs = slice(g * Hpg, (g + 1) * Hpg)   # R8
                 bs = None if bs_rows is None else bs_rows[n, g]
-                o, sel, tg, bs = _row(q[t, hs], k[g], v[g], q_idx[t, g], k_idx, t, top_k,
-                                      block, scale, bs)
+                o, sel, tg, bs, ls = _row(q[t, hs], k[g], v[g], q_idx[t, g], k_idx, t, top_k,
+                                          block, scale, bs)
                 out[i, hs] = o
+                lse[i, hs] = ls
                 sel_all[i][g] = sel
                 tie[i, g] = tg
                 if bs is not None:
                     scores[(i, g)] = bs
-    return dict(out=out, sel=sel_all, near_tie=tie, block_scores=scores, rows=rows)
+    return dict(out=out, lse=lse, sel=sel_all, near_tie=tie, block_scores=scores, rows=rows)
 
 
 def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
@@ -243,7 +254,7 @@ def decode(q, k_cache, v_cache, q_idx, k_idx, seq_lens, top_k: int,
         for g in range(G):
             hs = slice(g * Hpg, (g + 1) * Hpg)
             bs = None if bs_all is None else bs_all[g]
-            o, sel, tg, bs = _row(q[bi, hs], k_cache[bi, g], v_cache[bi, g], q_idx[bi, g],
+            o, sel, tg, bs, _ = _row(q[bi, hs], k_cache[bi, g], v_cache[bi, g], q_idx[bi, g],
                                   k_idx[bi], t, top_k, block, scale, bs)
             out[bi, hs] = o
             sel_all[bi][g] = sel

@@ -88,6 +88,13 @@ def test_dense_equivalence_library(T, G, Hpg, D, d_idx):
     ref = _sdpa(x["q"], x["k"], x["v"], causal=True)
     assert np.max(np.abs(res["out"] - ref)) < 1e-12
     assert np.max(np.abs(orc.dense_prefill(x["q"], x["k"], x["v"]) - ref)) < 1e-12
+    # the normaliser: torch.logsumexp over the full causal score matrix of each head
+    q = torch.as_tensor(orc.as_f64(x["q"]))
+    k = torch.as_tensor(orc.as_f64(x["k"]))
+    s = torch.einsum("thd,hjd->htj", q, k.repeat_interleave(Hpg, dim=0)) / math.sqrt(D)
+    causal = torch.ones(T, T, dtype=torch.bool).tril()
+    ref_lse = torch.logsumexp(s.masked_fill(~causal, float("-inf")), dim=2).T.numpy()
+    assert np.max(np.abs(res["lse"] - ref_lse)) < 1e-11
 
 
 def test_local_only_equals_block_diagonal_mask():
@@ -118,6 +125,13 @@ def test_sparse_equals_masked_attention():
     ref = _sdpa(x["q"], x["k"], x["v"], mask=mask)
     assert np.max(np.abs(res["out"] - ref)) < 1e-12
     assert any(len(res["sel"][t][0]) == 3 for t in range(T))
+    # lse: torch.logsumexp of the masked score matrix (catches a normaliser over the wrong
+    # token set, e.g. the unselected or future keys)
+    q = torch.as_tensor(orc.as_f64(x["q"]))
+    k = torch.as_tensor(orc.as_f64(x["k"]))
+    s = torch.einsum("thd,hjd->htj", q, k.repeat_interleave(Hpg, dim=0)) / math.sqrt(32)
+    ref_lse = torch.logsumexp(s.masked_fill(~torch.as_tensor(mask), float("-inf")), dim=2).T
+    assert np.max(np.abs(res["lse"] - ref_lse.numpy())) < 1e-11
 
 
 # -- Selection invariants, brute force over every row --------------------------------
