@@ -257,6 +257,10 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
 
   if (!decode) {
     if (lane < 16) lsum_s[lane] = l_run;
+    // lanes h < 16 hold head h's running maximum (log2 units) and sum
+    if (sparse && p.lse != nullptr && lane < Hpg)
+      p.lse[(p.q_begin + i) * Hq + (int64_t)g * Hpg + lane] =
+          l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     __syncthreads();
     elem* orow = (elem*)p.out + ((p.q_begin + i) * Hq + (int64_t)g * Hpg) * kHeadDim + 2 * lane;
 #pragma unroll

@@ -783,8 +783,9 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ shared, const typename E::elem* __restrict__ part_o,
-    const float* __restrict__ part_ml, typename E::elem* __restrict__ out, int G, int Hpg,
-    int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len) {
+    const float* __restrict__ part_ml, typename E::elem* __restrict__ out,
+    float* __restrict__ lse, int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
+    int64_t seq_len) {
   typedef typename E::elem elem;
   typedef TileOps<E> T;
   constexpr int kBufs = 1;  // fp32 path: one staged block
@@ -956,6 +957,9 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
     }
     if (ok_r[rt]) {
       const float inv = l_r[rt] > 0.f ? 1.f / l_r[rt] : 0.f;
+      if (lse != nullptr && q == 0)
+        lse[t_r[rt] * Hq + (int64_t)g * Hpg + h] =
+            l_r[rt] > 0.f ? (m_r[rt] + log2f(l_r[rt])) * kLn2 : -INFINITY;
       elem* dst = out + (t_r[rt] * Hq + (int64_t)g * Hpg + h) * kHeadDim;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -987,8 +991,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ shared, const uint16_t* __restrict__ part_o,
-    const float* __restrict__ part_ml, uint16_t* __restrict__ out, int G, int Hpg, int top_k,
-    int64_t q_begin, int64_t q_count, int64_t seq_len) {
+    const float* __restrict__ part_ml, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len) {
   typedef TileOps<BF16> T;
   // two buffers per operand as distinct arrays: with the block loop unrolled by two every
   // access names its buffer, so the compiler can tell that the loads of block j + 1 do
@@ -1141,6 +1145,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
   // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
   // them: each load instruction covers whole cache lines).
+  float m_fin = m_run;  // the reference maximum of l_run once the partials are in
   if (__ballot(myrare != 0)) {
     const int64_t prow0 = (irow * G + g) * top_k * Hpg + h;
     const float2* ml2 = reinterpret_cast<const float2*>(part_ml);
@@ -1148,6 +1153,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < KMAX; ++s2)
       if ((myrare >> s2) & 1ull) M = fmaxf(M, ml2[prow0 + (int64_t)s2 * Hpg].x);
+    m_fin = M;
     const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
     l_run *= a;
 #pragma unroll
@@ -1179,6 +1185,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   }
   if (ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (lse != nullptr && q == 0)
+      lse[t * Hq + (int64_t)g * Hpg + h] = l_run > 0.f ? (m_fin + log2f(l_run)) * kLn2 : -INFINITY;
     uint16_t* dst = out + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -1349,7 +1357,8 @@ size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, 
 
 template <class E>
 static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
-                              const int32_t* block_idx, void* out, void* ws, int G, int Hpg,
+                              const int32_t* block_idx, void* out, float* lse, void* ws, int G,
+                              int Hpg,
                               int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,
                               int nblk, hipStream_t st) {
   typedef typename E::elem elem;
@@ -1390,31 +1399,33 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
     if (top_k <= 16)
       hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(512), 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
-                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
+                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, lse, G, Hpg,
+                         top_k,
                          q_begin, q_count, seq_len);
     else
       hipLaunchKernelGGL((qtile_attn_bf16_kernel<64>), dim3((unsigned)npairs), dim3(512), 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
-                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, G, Hpg, top_k,
+                         shared, (const uint16_t*)part_o, part_ml, (uint16_t*)out, lse, G, Hpg,
+                         top_k,
                          q_begin, q_count, seq_len);
   }
   if constexpr (!E::is_bf16)
     hipLaunchKernelGGL((qtile_attn_kernel<E>), dim3((unsigned)npairs), dim3(512), 0, st,
                        (const elem*)q, (const elem*)k, (const elem*)v, block_idx, shared,
-                       (const elem*)part_o, part_ml, (elem*)out, G, Hpg, top_k, q_begin, q_count,
-                       seq_len);
+                       (const elem*)part_o, part_ml, (elem*)out, lse, G, Hpg, top_k, q_begin,
+                       q_count, seq_len);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_prefill(int bf16, const void* q, const void* k, const void* v,
-                             const int32_t* block_idx, void* out, void* workspace, int G, int Hpg,
-                             int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,
-                             int nblk, hipStream_t stream) {
+                             const int32_t* block_idx, void* out, float* lse, void* workspace,
+                             int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
+                             int64_t seq_len, int nblk, hipStream_t stream) {
   if (bf16)
-    return launch_kv_t<BF16>(q, k, v, block_idx, out, workspace, G, Hpg, top_k, q_begin, q_count,
-                             seq_len, nblk, stream);
-  return launch_kv_t<F32>(q, k, v, block_idx, out, workspace, G, Hpg, top_k, q_begin, q_count,
-                          seq_len, nblk, stream);
+    return launch_kv_t<BF16>(q, k, v, block_idx, out, lse, workspace, G, Hpg, top_k, q_begin,
+                             q_count, seq_len, nblk, stream);
+  return launch_kv_t<F32>(q, k, v, block_idx, out, lse, workspace, G, Hpg, top_k, q_begin,
+                          q_count, seq_len, nblk, stream);
 }
 
 }  // namespace msa

@@ -36,7 +36,6 @@ namespace msa {
 constexpr int kUnit = 256;                        // sorted entries per unit at most
 constexpr int kRowBytes = kHeadDim * 2;           // one bf16 row of 128 values
 constexpr int kWaveTile = 32 * kRowBytes;         // 32 rows (one wave's entries)
-constexpr float kLn2 = 0.6931471805599453f;
 
 __global__ void kl_unit_count_kernel(const int32_t* __restrict__ offset, int64_t nb,
                                      int32_t* __restrict__ unit_off) {

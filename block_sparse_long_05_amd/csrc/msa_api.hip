@@ -219,13 +219,14 @@ msa_status msa_index_topk(const msa_problem* p, const void* q_idx, const void* k
 }
 
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
-                                   const void* v, const int32_t* block_idx, void* out,
+                                   const void* v, const int32_t* block_idx, void* out, float* lse,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   msa_status st = check_problem(p);
   if (st != MSA_OK) return st;
   if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) || !aligned16(out))
     return MSA_ERR_INVALID_ARGUMENT;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MSA_ERR_INVALID_ARGUMENT;
   if (p->q_count == 0) return MSA_OK;
   // KV-centric when asked for, or by default when the caller's workspace can hold it.
   bool kv = p->algo == MSA_ALGO_KV_CENTRIC;
@@ -239,7 +240,7 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   }
   if (kv) {
     if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
-    return hip_status(launch_kv_prefill(p->dtype == MSA_DTYPE_BF16, q, k, v, block_idx, out,
+    return hip_status(launch_kv_prefill(p->dtype == MSA_DTYPE_BF16, q, k, v, block_idx, out, lse,
                                         workspace, p->num_groups, p->heads_per_group, p->top_k,
                                         p->q_begin, p->q_count, p->seq_len, (int)nblk_of(p),
                                         as_stream(stream)));
@@ -252,6 +253,7 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   gp.v = v;
   gp.block_idx = block_idx;
   gp.out = out;
+  gp.lse = lse;
   gp.G = p->num_groups;
   gp.Hpg = p->heads_per_group;
   gp.top_k = p->top_k;

@@ -19,6 +19,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 128;
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // ---- bf16 storage is raw uint16_t --------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

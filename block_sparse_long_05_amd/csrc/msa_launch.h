@@ -58,6 +58,7 @@ struct GatherParams {
   const void* v;
   const int32_t* block_idx;  // sparse modes
   void* out;                 // prefill: final output
+  float* lse;                // sparse prefill: per (row, head) ln of the softmax normaliser, or null
   float* part_o;             // decode: [units][Hpg][128] unnormalised partial outputs
   float* part_ml;            // decode: [units][Hpg][2] (running max in log2 units, sum)
   int G, Hpg, top_k;
@@ -105,8 +106,8 @@ hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_i
                                    int64_t seq_len, int nblk, hipStream_t st);
 
 hipError_t launch_kv_prefill(int bf16, const void* q, const void* k, const void* v,
-                             const int32_t* block_idx, void* out, void* workspace, int G, int Hpg,
-                             int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len,
-                             int nblk, hipStream_t stream);
+                             const int32_t* block_idx, void* out, float* lse, void* workspace,
+                             int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
+                             int64_t seq_len, int nblk, hipStream_t stream);
 
 }  // namespace msa

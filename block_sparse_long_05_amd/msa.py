@@ -72,7 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_scores.argtypes = [pp, vp, vp, vp, vp]
     lib.msa_block_topk.argtypes = [pp, vp, vp, vp]
     lib.msa_index_topk.argtypes = [pp, vp, vp, vp, vp]
-    lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
     i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -210,10 +210,12 @@ def index_topk_supported(p: Problem) -> bool:
     return p.mode == "prefill" and p.dtype == "bf16" and p.top_k <= 16
 
 
-def msa_sparse_attn_prefill(p: Problem, q, k, v, block_idx, out, workspace=None, stream=None):
+def msa_sparse_attn_prefill(p: Problem, q, k, v, block_idx, out, workspace=None, stream=None,
+                            lse=None):
+    """lse (optional, fp32 [T, Hq]) receives each row's and head's ln softmax normaliser."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().msa_sparse_attn_prefill(
-        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out),
+        ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_prefill")
 
 
@@ -264,9 +266,10 @@ def alloc_block_idx(p: Problem, device="cuda") -> torch.Tensor:
 
 def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None,
             algo: str = "auto", out=None, block_scores=None, block_idx=None, workspace=None,
-            stream=None, index: str = "separate"):
+            stream=None, index: str = "separate", lse=None):
     """MSA prefill of query rows [q_begin, q_begin + q_count): index scores -> top-k ->
-    sparse attention. x holds q, k, v, q_idx, k_idx on the device. index="fused" runs the
+    sparse attention. x holds q, k, v, q_idx, k_idx on the device; lse (fp32 [T, Hq]), when
+    given, receives the rows' softmax normalisers. index="fused" runs the
     index branch as msa_index_topk (no block scores; block_scores is returned as None).
     Returns (out, block_idx, block_scores)."""
     q = x["q"]
@@ -293,7 +296,7 @@ def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None
             block_scores = alloc_block_scores(p, q.device)
         msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
         msa_block_topk(p, block_scores, block_idx, stream)
-    msa_sparse_attn_prefill(p, q, x["k"], x["v"], block_idx, out, workspace, stream)
+    msa_sparse_attn_prefill(p, q, x["k"], x["v"], block_idx, out, workspace, stream, lse=lse)
     return out, block_idx, block_scores
 
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 #define MSA_BLOCK_SIZE 128
 #define MSA_HEAD_DIM 128
 #define MSA_MAX_TOPK 64
@@ -143,11 +143,14 @@ msa_status msa_index_topk(const msa_problem* p, const void* q_idx, const void* k
  *   out[t, h] = sum_j softmax_j(q[t, h] . k[g, j] / sqrt(D)) v[g, j]
  * over the tokens j <= t of the blocks listed in block_idx[i, g, :]. Ids < 0 are
  * padding; ids above the query's local block are ignored. Writes out rows
- * [q_begin, q_begin + q_count). workspace may be NULL when
+ * [q_begin, q_begin + q_count). lse may be NULL; otherwise it is fp32 [T, Hq] (4-byte
+ * aligned) and receives, for the same rows, lse[t, h] = ln sum_j exp(q[t, h] . k[g, j] /
+ * sqrt(D)) over the same tokens (the softmax normaliser a backward pass or the index-branch
+ * KL loss needs; -inf for a row with no visible kept token). workspace may be NULL when
  * msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_PREFILL) is 0 for the chosen algo.
  */
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
-                                   const void* v, const int32_t* block_idx, void* out,
+                                   const void* v, const int32_t* block_idx, void* out, float* lse,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*

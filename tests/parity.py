@@ -13,6 +13,9 @@ import torch
 from oracle import msa_oracle as orc
 
 OUT_TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+# Softmax normalisers ln sum exp(s / sqrt(D)): fp32 logits of exact products (bf16) or fp32
+# MFMA (fp32), fp32 sums of fp32 exponentials; absolute errors are ~1e-6 on values ~10.
+LSE_TOL = 1e-4
 # Block scores: fp32 accumulation of d_idx products against the fp64 oracle.
 SCORE_RTOL = 2e-5
 
@@ -45,7 +48,7 @@ def check_selection(idx_gpu, oracle_sel, near_tie, top_k, label=""):
 
 
 def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, out_offset=0,
-                  label=""):
+                  label="", lse_gpu=None):
     """Compare a prefill run for oracle rows `rows` (absolute token ids). idx_gpu and
     bs_gpu start at row q_begin, out_gpu at row out_offset."""
     dtype = x["q"].dtype
@@ -66,7 +69,16 @@ def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, out_
                                              idx_rows[i, g], t)
     err = float(np.max(np.abs(got - ref)))
     assert err <= tol, f"{label}: max abs err {err} > {tol}"
-    return dict(err=err, near_ties=int(res["near_tie"].sum()), differ=len(differ))
+    info = dict(err=err, near_ties=int(res["near_tie"].sum()), differ=len(differ))
+    if lse_gpu is not None:  # rows whose selection differs (near ties) are left out
+        keep = np.ones((len(rows), G), dtype=bool)
+        for (i, g) in differ:
+            keep[i, g] = False
+        keep = np.repeat(keep, Hpg, axis=1)
+        lerr = np.abs(lse_gpu[rows - out_offset].astype(np.float64) - res["lse"])[keep]
+        info["lse_err"] = float(lerr.max()) if lerr.size else 0.0
+        assert info["lse_err"] <= LSE_TOL, f"{label}: lse max abs err {info['lse_err']}"
+    return info
 
 
 def check_decode(x, out_gpu, idx_gpu, bs_gpu, res, top_k, label=""):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msa.load_library()
-    assert lib.msa_abi_version() == 1
+    assert lib.msa_abi_version() == 2
     for s in range(5):
         assert msa.status_string(s).startswith("MSA_")
 
@@ -82,15 +82,18 @@ def test_bad_enums_and_null_pointers():
     assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
     c = p.c()
     c.algo = 9
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0) \
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0) \
         == msa.MSA_ERR_INVALID_ARGUMENT
     assert lib.msa_index_scores(None, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
     c = p.c()
     assert lib.msa_index_scores(ctypes.byref(c), 0, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
     assert lib.msa_index_scores(ctypes.byref(c), FAKE + 2, FAKE, FAKE, 0) \
         == msa.MSA_ERR_INVALID_ARGUMENT
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0) \
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0, 0) \
         == msa.MSA_ERR_INVALID_ARGUMENT
+    # lse is optional, but when given it must be 4-byte aligned
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 0,
+                                       0, 0) == msa.MSA_ERR_INVALID_ARGUMENT
 
 
 def test_mode_mismatch_rejected():
@@ -140,7 +143,7 @@ def test_empty_chunk_is_a_no_op():
     c = _prefill(q_begin=4096, q_count=0).c()
     assert lib.msa_index_scores(ctypes.byref(c), FAKE, FAKE, FAKE, 0) == msa.MSA_OK
     assert lib.msa_block_topk(ctypes.byref(c), FAKE, FAKE, 0) == msa.MSA_OK
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0) \
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0) \
         == msa.MSA_OK
 
 

@@ -32,11 +32,19 @@ def _oracle_prefill(key, x, top_k, rows=None):
     return _ORACLE[key]
 
 
+_LAST_LSE = {}
+
+
 def _run_prefill(x, top_k, q_begin=0, q_count=None, algo="auto"):
+    """Runs the prefill with the optional lse output; the lse (NaN outside the chunk) is
+    kept in _LAST_LSE["lse"]."""
     xd = _to(x)
     out = torch.zeros_like(xd["q"])
-    out, idx, bs = msa.prefill(xd, top_k, q_begin=q_begin, q_count=q_count, algo=algo, out=out)
+    lse = torch.full(xd["q"].shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    out, idx, bs = msa.prefill(xd, top_k, q_begin=q_begin, q_count=q_count, algo=algo, out=out,
+                               lse=lse)
     torch.cuda.synchronize()
+    _LAST_LSE["lse"] = parity.np32(lse)
     return parity.np32(out), idx.cpu().numpy(), parity.np32(bs)
 
 
@@ -58,7 +66,8 @@ def test_prefill_parity(T, G, Hpg, d_idx, top_k, dtype, planted, algo):
     print(f"prefill parity T={T} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k} {dtype} {algo}", flush=True)
     out, idx, bs = _run_prefill(x, top_k, algo=algo)
     res = _oracle_prefill((T, G, Hpg, d_idx, top_k, dtype, planted), x, top_k)
-    info = parity.check_prefill(x, np.arange(T), out, idx, bs, res, top_k, label=f"T={T}")
+    info = parity.check_prefill(x, np.arange(T), out, idx, bs, res, top_k, label=f"T={T}",
+                                lse_gpu=_LAST_LSE["lse"])
     print(info)
 
 
@@ -71,8 +80,11 @@ def test_prefill_chunked_rows(algo):
     out, idx, bs = _run_prefill(x, top_k, q_begin=q0, q_count=qn, algo=algo)
     rows = np.arange(q0, q0 + qn)
     res = _oracle_prefill("chunk", x, top_k, rows=rows)
-    parity.check_prefill(x, rows, out, idx, bs, res, top_k, q_begin=q0, label="chunk")
+    lse = _LAST_LSE["lse"]
+    parity.check_prefill(x, rows, out, idx, bs, res, top_k, q_begin=q0, label="chunk",
+                         lse_gpu=lse)
     assert np.all(out[:q0] == 0) and np.all(out[q0 + qn:] == 0)
+    assert np.isnan(lse[:q0]).all() and np.isnan(lse[q0 + qn:]).all()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
