@@ -385,6 +385,31 @@ def run_kl(name, cfg, args, torch, msa, x, idx_full, chunks, T, G, Hpg, d_idx, t
     kl_ms = time_reps(torch, kl_step, max(1, args.steps // 2))
     fl = kl_flops(T, G, Hpg, 128, d_idx, top_k)
     tf = fl / (kl_ms * 1e-3) / 1e12
+    # the same with the main heads' normalisers from the forward attention's lse output
+    # (what a training step has anyway); the attention itself is not timed here
+    main_lse = torch.empty((T, G * Hpg), dtype=torch.float32, device="cuda")
+    aprobs = [msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                          index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n)
+              for c0, n in chunks]
+    aws = torch.empty(max(msa.msa_workspace_size(p, "sparse_attn_prefill") for p in aprobs),
+                      dtype=torch.uint8, device="cuda")
+    aout = torch.empty_like(x["q"])
+    for p, (c0, n) in zip(aprobs, chunks):
+        msa.msa_sparse_attn_prefill(p, x["q"], x["k"], x["v"], idx_full[c0:c0 + n], aout, aws,
+                                    lse=main_lse)
+    del aws, aout
+    loss_ref = loss.clone()
+
+    def kl_step_lse():
+        dk.zero_()
+        for p, (c0, n) in zip(kprobs, chunks):
+            msa.msa_index_kl_prefill(p, x["q"], x["k"], x["q_idx"], x["k_idx"],
+                                     idx_full[c0:c0 + n], scale, loss[c0:c0 + n], dq[c0:c0 + n],
+                                     dk, kws, main_lse=main_lse)
+    kl_lse_ms = time_reps(torch, kl_step_lse, max(1, args.steps // 2))
+    tf_lse = fl / (kl_lse_ms * 1e-3) / 1e12
+    lse_loss_diff = float((loss - loss_ref).abs().max())
+    del main_lse
     # identities of the gradients at full size (fp64 on the device): each row's score
     # gradients sum to zero, and sum_j dk[j] . k_idx[j] = sum_(t,g) dq[t,g] . q_idx[t,g]
     dk64 = dk.double()
@@ -392,10 +417,13 @@ def run_kl(name, cfg, args, torch, msa, x, idx_full, chunks, T, G, Hpg, d_idx, t
     rhs = float((dq.double() * x["q_idx"].double()).sum())
     zero_rel = float(dk64.sum(0).abs().max() / dk64.abs().sum(0).max())
     out = dict(ms=kl_ms, tflops=tf, frac_of_peak=tf / peak, flops=fl, index_scale=scale,
+               with_main_lse=dict(ms=kl_lse_ms, tflops=tf_lse, frac_of_peak=tf_lse / peak,
+                                  max_loss_diff_vs_standalone=lse_loss_diff),
                loss_mean=float(loss.double().mean()), dk_sum_rel=zero_rel,
                identity_rel=abs(lhs - rhs) / max(abs(lhs), abs(rhs), 1e-30))
     log(f"[{name}] index KL loss+grad {kl_ms:.2f} ms ({tf:.0f} TFLOP/s, "
-        f"{tf / peak * 100:.1f}% of peak)  mean loss {out['loss_mean']:.4f}  "
+        f"{tf / peak * 100:.1f}% of peak); with the attention's lse {kl_lse_ms:.2f} ms "
+        f"({tf_lse:.0f} TFLOP/s, loss diff {lse_loss_diff:.1e})  mean loss {out['loss_mean']:.4f}  "
         f"sum dk rel {zero_rel:.2e}  identity rel {out['identity_rel']:.2e}")
     del kws, loss, dq, dk
     torch.cuda.empty_cache()

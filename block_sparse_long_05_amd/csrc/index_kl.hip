@@ -16,7 +16,9 @@
 // block's K (row swizzle) and index keys (V swizzle) in LDS once. Two passes over the units:
 //   pass 0: per entry, a partial (max, sum of exponentials) for each head and for the
 //           index scores over the block's visible keys; a fold turns a row's partials into
-//           log-sum-exps (log2 units) in slot order;
+//           log-sum-exps (log2 units) in slot order. When the caller passes the main heads'
+//           log-sum-exps (the forward attention computes them anyway), only the index
+//           scores are reduced here;
 //   pass 1: per entry, P (head mean, from the row's log-sum-exps) and I for the block's
 //           keys, the entry's loss term, its dq_idx partial (K_idx^T . W^T, the transpose
 //           read of the main branch's PV product) and, per unit, the dk_idx partial of the
@@ -57,8 +59,9 @@ __device__ __forceinline__ void load_row_op(u32x4* op, const uint16_t* row, int 
     op[s] = ok ? *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Pass 0 (kGrad false) or pass 1 (kGrad true) over one unit.
-template <bool kGrad>
+// Pass 0 (kGrad false) or pass 1 (kGrad true) over one unit. kIndexOnly: pass 0 with the
+// main heads' log-sum-exps given by the caller, so only the index scores are reduced.
+template <bool kGrad, bool kIndexOnly = false>
 __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ QI, const uint16_t* __restrict__ KI,
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
   const int e0 = offset[k] + kUnit * (u - unit_off[k]);
   const int n = min(kUnit, offset[k + 1] - e0);
   if (tid < n) ids[tid] = sorted[e0 + tid];
-  k_block_dma<256>(K, g, c, seq_len, Kb, tid);
+  if constexpr (!kIndexOnly) k_block_dma<256>(K, g, c, seq_len, Kb, tid);
   k_block_dma<256, true>(KI, 0, c, seq_len, KIb, tid);
   MSA_WAIT_VMCNT(0);
   __syncthreads();
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
       auto visible = [&](int kt, int r) { return ok && 32 * kt + 8 * (r >> 2) + (r & 3) <= limq; };
 
       if constexpr (!kGrad) {
-        for (int h = 0; h <= Hpg; ++h) {
+        for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
           u32x4 qop[kHeadDim / 16];
           if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q, ok);
           const float sc = h < Hpg ? c_main : c_idx;
@@ -247,14 +250,22 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
 
 // Row log-sum-exps (log2 units) of the main heads and the index scores from the partials of
 // the row's visible entries, combined in slot order. -inf for a row without any.
+// With main_lse (ln units, [T, G * Hpg]) the main heads' values are taken from it.
 __global__ void kl_stats_fold_kernel(const int32_t* __restrict__ block_idx,
-                                     const float* __restrict__ part_stats, float* __restrict__ lse,
+                                     const float* __restrict__ part_stats,
+                                     const float* __restrict__ main_lse, float* __restrict__ lse,
                                      int64_t rows_g, int G, int Hpg, int top_k, int64_t q_begin) {
   const int H1 = Hpg + 1;
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < rows_g * H1;
        x += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rg = x / H1;
     const int h = (int)(x - rg * H1);
+    if (main_lse != nullptr && h < Hpg) {
+      const int64_t t = q_begin + rg / G;
+      const int g = (int)(rg % G);
+      lse[rg * H1 + h] = main_lse[(t * G + g) * Hpg + h] * kLog2e;
+      continue;
+    }
     const int64_t b = (q_begin + rg / G) / kBlock;
     float m = -INFINITY;
     for (int s = 0; s < top_k; ++s) {
@@ -342,7 +353,8 @@ size_t kl_workspace_bytes(int64_t q_count, int G, int Hpg, int top_k, int nblk) 
 }
 
 hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_idx,
-                                   const void* k_idx, const int32_t* block_idx, float index_scale,
+                                   const void* k_idx, const int32_t* block_idx,
+                                   const float* main_lse, float index_scale,
                                    float* loss, float* dq_idx, float* dk_idx, void* workspace,
                                    int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
                                    int64_t seq_len, int nblk, hipStream_t st) {
@@ -378,13 +390,18 @@ hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_i
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* QI = static_cast<const uint16_t*>(q_idx);
   const uint16_t* KI = static_cast<const uint16_t*>(k_idx);
-  hipLaunchKernelGGL((kl_unit_kernel<false>), dim3((unsigned)U), dim3(256), 0, st, Q, K, QI, KI,
-                     sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k, q_begin,
-                     seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
+  if (main_lse != nullptr)
+    hipLaunchKernelGGL((kl_unit_kernel<false, true>), dim3((unsigned)U), dim3(256), 0, st, Q, K,
+                       QI, KI, sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k,
+                       q_begin, seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
+  else
+    hipLaunchKernelGGL((kl_unit_kernel<false>), dim3((unsigned)U), dim3(256), 0, st, Q, K, QI, KI,
+                       sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k, q_begin,
+                       seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
   const int64_t rows_g = q_count * G;
   const unsigned grid_s = (unsigned)std::min<int64_t>((rows_g * (Hpg + 1) + 255) / 256, 65536);
   hipLaunchKernelGGL(kl_stats_fold_kernel, dim3(grid_s), dim3(256), 0, st, block_idx, part_stats,
-                     lse, rows_g, G, Hpg, top_k, q_begin);
+                     main_lse, lse, rows_g, G, Hpg, top_k, q_begin);
   hipLaunchKernelGGL((kl_unit_kernel<true>), dim3((unsigned)U), dim3(256), 0, st, Q, K, QI, KI,
                      sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k, q_begin,
                      seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);

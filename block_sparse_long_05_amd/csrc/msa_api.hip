@@ -265,8 +265,9 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
 
 msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void* k,
                                 const void* q_idx, const void* k_idx, const int32_t* block_idx,
-                                float index_scale, float* loss, float* dq_idx, float* dk_idx,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                const float* main_lse, float index_scale, float* loss,
+                                float* dq_idx, float* dk_idx, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   msa_status st = check_problem(p);
   if (st != MSA_OK) return st;
   if (p->mode != MSA_MODE_PREFILL || p->dtype != MSA_DTYPE_BF16 || p->index_dim != 128)
@@ -275,10 +276,13 @@ msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
       !aligned16(block_idx) || !aligned16(loss) || !aligned16(dq_idx) || !aligned16(dk_idx))
     return MSA_ERR_INVALID_ARGUMENT;
+  if (main_lse != nullptr && (reinterpret_cast<uintptr_t>(main_lse) & 3u) != 0)
+    return MSA_ERR_INVALID_ARGUMENT;
   if (p->q_count == 0) return MSA_OK;
   if (workspace_bytes < kl_ws_bytes(p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_index_kl_prefill(q, k, q_idx, k_idx, block_idx, index_scale, loss,
+  return hip_status(launch_index_kl_prefill(q, k, q_idx, k_idx, block_idx, main_lse, index_scale,
+                                            loss,
                                             dq_idx, dk_idx, workspace, p->num_groups,
                                             p->heads_per_group, p->top_k, p->q_begin, p->q_count,
                                             p->seq_len, (int)nblk_of(p), as_stream(stream)));

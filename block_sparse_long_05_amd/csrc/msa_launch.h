@@ -100,7 +100,8 @@ void launch_exclusive_scan(int32_t* a, int64_t n, hipStream_t st);
 // Index-branch KL loss and gradients (index_kl.hip), bf16, D = d_idx = 128.
 size_t kl_workspace_bytes(int64_t q_count, int G, int Hpg, int top_k, int nblk);
 hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_idx,
-                                   const void* k_idx, const int32_t* block_idx, float index_scale,
+                                   const void* k_idx, const int32_t* block_idx,
+                                   const float* main_lse, float index_scale,
                                    float* loss, float* dq_idx, float* dk_idx, void* workspace,
                                    int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count,
                                    int64_t seq_len, int nblk, hipStream_t st);

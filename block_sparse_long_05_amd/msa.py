@@ -78,8 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.msa_index_scores_paged.argtypes = [pp, vp, vp, vp, i32, i64, vp, vp]
     lib.msa_sparse_attn_decode_paged.argtypes = [pp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]
-    lib.msa_index_kl_prefill.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
-                                         sz, vp]
+    lib.msa_index_kl_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                         vp, sz, vp]
     lib.msa_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(sz)]
     lib.msa_status_string.argtypes = [ctypes.c_int]
     lib.msa_status_string.restype = ctypes.c_char_p
@@ -228,14 +228,15 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, block_idx, out, work
 
 
 def msa_index_kl_prefill(p: Problem, q, k, q_idx, k_idx, block_idx, index_scale: float, loss,
-                         dq_idx, dk_idx, workspace=None, stream=None):
+                         dq_idx, dk_idx, workspace=None, stream=None, main_lse=None):
     """Index-branch KL loss (loss [q_count, G], dq_idx [q_count, G, 128] written) and its
-    index-key gradient (ADDED into dk_idx [T, 128]); all three fp32."""
+    index-key gradient (ADDED into dk_idx [T, 128]); all three fp32. main_lse: the lse that
+    msa_sparse_attn_prefill wrote for the same selection (optional)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().msa_index_kl_prefill(
         ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx), _ptr(block_idx),
-        float(index_scale), _ptr(loss), _ptr(dq_idx), _ptr(dk_idx), _ptr(workspace), ws_bytes,
-        _stream(stream)), "msa_index_kl_prefill")
+        _ptr(main_lse), float(index_scale), _ptr(loss), _ptr(dq_idx), _ptr(dk_idx),
+        _ptr(workspace), ws_bytes, _stream(stream)), "msa_index_kl_prefill")
 
 
 def msa_dense_gqa_attn(p: Problem, q, k, v, out, workspace=None, stream=None):
@@ -301,7 +302,8 @@ def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None
 
 
 def index_kl(x: dict, block_idx, top_k: int, index_scale: float, q_begin: int = 0,
-             q_count: Optional[int] = None, dk_idx=None, workspace=None, stream=None):
+             q_count: Optional[int] = None, dk_idx=None, workspace=None, stream=None,
+             main_lse=None):
     """Index-branch KL loss and gradients for query rows [q_begin, q_begin + q_count) on the
     selection block_idx [q_count, G, top_k]. x holds q, k, q_idx, k_idx (bf16) on the device.
     dk_idx (fp32 [T, 128]) is accumulated into; a zeroed one is made when it is None.
@@ -321,7 +323,7 @@ def index_kl(x: dict, block_idx, top_k: int, index_scale: float, q_begin: int = 
     if workspace is None:
         workspace = alloc_workspace(p, "index_kl", q.device)
     msa_index_kl_prefill(p, q, x["k"], x["q_idx"], x["k_idx"], block_idx, index_scale, loss, dq,
-                         dk_idx, workspace, stream)
+                         dk_idx, workspace, stream, main_lse=main_lse)
     return loss, dq, dk_idx
 
 

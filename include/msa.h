@@ -208,12 +208,16 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, con
  * index_scale must be finite and > 0 (else MSA_ERR_INVALID_ARGUMENT). Loss and dq_idx are
  * bit-identical from run to run; dk_idx sums each block's entries in the order the
  * reverse index places them, which may vary from run to run at the level of fp32 rounding.
+ * main_lse may be NULL; otherwise it is the fp32 [T, Hq] lse that msa_sparse_attn_prefill
+ * wrote for the same rows and block_idx (ln of each head's softmax normaliser), and the main
+ * heads' normalisers are taken from it instead of being recomputed (4-byte aligned).
  * Workspace: msa_workspace_size(p, MSA_ENTRY_INDEX_KL).
  */
 msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void* k,
                                 const void* q_idx, const void* k_idx, const int32_t* block_idx,
-                                float index_scale, float* loss, float* dq_idx, float* dk_idx,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                const float* main_lse, float index_scale, float* loss,
+                                float* dq_idx, float* dk_idx, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Dense GQA attention with the same heads (the baseline the researchpapers.dev summary

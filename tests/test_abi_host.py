@@ -202,14 +202,15 @@ def test_index_kl_validation():
                                   ctypes.byref(n)) == msa.MSA_OK and n.value > 0
     args = (FAKE, FAKE, FAKE, FAKE, FAKE)
 
-    def call(p, scale=0.1, ws=n.value, loss=FAKE):
-        return lib.msa_index_kl_prefill(ctypes.byref(p.c()), *args, ctypes.c_float(scale), loss,
-                                        FAKE, FAKE, FAKE, ws, 0)
+    def call(p, scale=0.1, ws=n.value, loss=FAKE, main_lse=0):
+        return lib.msa_index_kl_prefill(ctypes.byref(p.c()), *args, main_lse, ctypes.c_float(scale),
+                                        loss, FAKE, FAKE, FAKE, ws, 0)
 
     for p in (_prefill(dtype="f32"), _prefill(index_dim=64)):
         assert call(p) == msa.MSA_ERR_UNSUPPORTED
-    assert lib.msa_index_kl_prefill(ctypes.byref(_decode()), *args, ctypes.c_float(0.1), FAKE,
+    assert lib.msa_index_kl_prefill(ctypes.byref(_decode()), *args, 0, ctypes.c_float(0.1), FAKE,
                                     FAKE, FAKE, FAKE, n.value, 0) == msa.MSA_ERR_UNSUPPORTED
+    assert call(ok, main_lse=FAKE + 2) == msa.MSA_ERR_INVALID_ARGUMENT
     for scale in (0.0, -1.0, float("inf"), float("nan")):
         assert call(ok, scale) == msa.MSA_ERR_INVALID_ARGUMENT
     assert call(ok, loss=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT

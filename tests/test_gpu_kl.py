@@ -26,6 +26,15 @@ def _dev(x):
     return {k: v.to(DEV) for k, v in x.items() if k in ("q", "k", "q_idx", "k_idx")}
 
 
+_ORACLE = {}
+
+
+def _oracle_cached(key, x, sel, scale):
+    if key not in _ORACLE:
+        _ORACLE[key] = orc.index_kl(x["q"], x["k"], x["q_idx"], x["k_idx"], sel, scale)
+    return _ORACLE[key]
+
+
 def _oracle(x, sel, scale, q_begin=0, rows=None):
     return orc.index_kl(x["q"], x["k"], x["q_idx"], x["k_idx"], sel, scale, q_begin=q_begin,
                         rows=rows)
@@ -47,7 +56,7 @@ def test_index_kl_matches_oracle(T, G, Hpg, top_k, popular, scale, seed):
     sel = synth.random_selection(T, G, top_k, seed=seed, popular_per_group=popular)
     loss, dq, dk = msa.index_kl(_dev(x), sel.to(DEV), top_k, scale)
     torch.cuda.synchronize()
-    ref = _oracle(x, sel.numpy(), scale)
+    ref = _oracle_cached((T, G, Hpg, top_k, popular, scale, seed), x, sel.numpy(), scale)
     print(parity.check_kl(parity.np32(loss), parity.np32(dq), ref, np.arange(T),
                           parity.np32(dk), label=f"T={T}"))
 
@@ -90,3 +99,28 @@ def test_index_kl_padding_and_invisible_ids():
     ref = _oracle(x, sel.numpy(), scale)
     parity.check_kl(parity.np32(loss), parity.np32(dq), ref, np.arange(T), parity.np32(dk),
                     label="padding")
+
+
+@pytest.mark.parametrize("algo", ["auto", "query_centric"])
+def test_index_kl_with_main_lse(algo):
+    """With the main heads' normalisers taken from msa_sparse_attn_prefill's lse output (same
+    selection), the loss and gradients still match the oracle and the standalone call."""
+    T, G, Hpg, top_k, scale = 2100, 8, 8, 16, 1.0 / math.sqrt(128)
+    print(f"index kl with main lse ({algo})", flush=True)
+    x = _inputs(T, G, Hpg, 2)
+    xd = _dev(x)
+    xd["v"] = x["v"].to(DEV)
+    sel = synth.random_selection(T, G, top_k, seed=2, popular_per_group=4)
+    seld = sel.to(DEV)
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                    index_dim=128, top_k=top_k, seq_len=T, q_begin=0, q_count=T, algo=algo)
+    lse = torch.empty((T, G * Hpg), dtype=torch.float32, device=DEV)
+    msa.msa_sparse_attn_prefill(p, xd["q"], xd["k"], xd["v"], seld, torch.empty_like(xd["q"]),
+                                msa.alloc_workspace(p, "sparse_attn_prefill"), lse=lse)
+    loss, dq, dk = msa.index_kl(xd, seld, top_k, scale, main_lse=lse)
+    loss0, dq0, dk0 = msa.index_kl(xd, seld, top_k, scale)
+    torch.cuda.synchronize()
+    ref = _oracle_cached((T, G, Hpg, top_k, 4, scale, 2), x, sel.numpy(), scale)
+    print(parity.check_kl(parity.np32(loss), parity.np32(dq), ref, np.arange(T),
+                          parity.np32(dk), label="main lse"))
+    assert float((loss - loss0).abs().max()) < 1e-4
