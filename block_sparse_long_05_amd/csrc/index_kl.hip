@@ -72,8 +72,8 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
     float* __restrict__ part_dq, float* __restrict__ part_dk) {
   __shared__ __align__(16) uint8_t Kb[kBlock * kRowBytes];
   __shared__ __align__(16) uint8_t KIb[kBlock * kRowBytes];
-  __shared__ __align__(16) uint8_t Wb[kGrad ? 4 * kWaveTile : 16];
-  __shared__ __align__(16) uint8_t QIb[kGrad ? 4 * kWaveTile : 16];
+  __shared__ __align__(16) uint8_t Wb[kGrad ? 4 * kWaveTile : 16];   // per wave: W tile
+  __shared__ __align__(16) uint8_t QIb[kGrad ? 4 * kWaveTile : 16];  // per wave: q_idx rows
   __shared__ int32_t ids[kUnit];
 
   const int tid = threadIdx.x;
@@ -109,11 +109,10 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
       const int64_t t = q_begin + rowg / G;
       // last visible key offset in the block, folded with the lane's key offset 4q
       const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock - 1);
-      const int limq = lim - 4 * q;
+      const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
       const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
       u32x4 qiop[kHeadDim / 16];
       load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
-      auto visible = [&](int kt, int r) { return ok && 32 * kt + 8 * (r >> 2) + (r & 3) <= limq; };
 
       if constexpr (!kGrad) {
         for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
@@ -122,13 +121,15 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
           const float sc = h < Hpg ? c_main : c_idx;
           f32x16 sv[4];
           float mx = -INFINITY;
+          int lq = limq;
+          asm volatile("" : "+v"(lq));
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             sv[kt] = h < Hpg ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
                              : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float x = visible(kt, r) ? sv[kt][r] * sc : -INFINITY;
+              const float x = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? sv[kt][r] * sc : -INFINITY;
               sv[kt][r] = x;
               mx = fmaxf(mx, x);
             }
@@ -156,28 +157,36 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
           u32x4 qop[kHeadDim / 16];
           load_row_op(qop, qrow + h * kHeadDim, q, ok);
           const float lh = ok ? lrow[h] : 0.f;
+          // the causal compares are redone per head (two VALU ops per score) rather than
+          // kept as 64 hoisted lane masks, which the compiler would spill
+          int lq = limq;
+          asm volatile("" : "+v"(lq));
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
             const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              w[kt][r] += visible(kt, r) ? fast_exp2(fmaf(sv[r], c_main, -lh)) : 0.f;
+            for (int r = 0; r < 16; ++r) {
+              const float e = fast_exp2(fmaf(sv[r], c_main, -lh));
+              w[kt][r] += 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? e : 0.f;
+            }
           }
         }
         const float inv_h = 1.f / (float)Hpg;
         const float li = ok ? lrow[Hpg] : 0.f;
         float lsum = 0.f;
+        int lq = limq;
+        asm volatile("" : "+v"(lq));
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           const f32x16 xv = s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const bool vis = visible(kt, r);
-            const float p = w[kt][r] * inv_h;
-            const float z = fmaf(xv[r], c_idx, -li);        // log2 I
+            const float p = w[kt][r] * inv_h;             // 0 for keys the row cannot see
+            const float z = fmaf(xv[r], c_idx, -li);      // log2 I
             const float iv = fast_exp2(z);
-            lsum += (vis && p > 0.f) ? p * (log2f(p) - z) : 0.f;
-            w[kt][r] = vis ? index_scale * (iv - p) : 0.f;
+            // P ln(P / I) in log2 units; p = 0 gives 0 (the clamp only keeps the log finite)
+            lsum += p * (__builtin_amdgcn_logf(fmaxf(p, 1e-30f)) - z);
+            w[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? index_scale * (iv - p) : 0.f;
           }
         }
         lsum += __shfl_xor(lsum, 32, 64);
