@@ -311,9 +311,173 @@ __global__ __launch_bounds__(64 * kLongWaves) void block_topk_long_kernel(
                lane);
 }
 
+// Decode rows (few rows, up to 8192 blocks each): one workgroup of 256 threads per row with
+// the whole row in registers, so every load is in flight at once and no step waits on
+// global memory twice:
+//   1. thread i holds the keys of blocks 4i .. 4i + 3, 4i + 1024 .. (16-byte loads; blocks
+//      i, i + 256, ... when rows are not 16-byte aligned) and their maximum; the K-th largest
+//      of the 256 thread maxima is a lower bound LB of the row's K-th largest key;
+//   2. keys >= LB go to LDS as 64-bit values (key << 32) | ~block, which are distinct and
+//      order the row exactly by the rule: higher score first, then lower block index;
+//   3. one wave keeps the K largest of those values (up to 256 candidates: each is kept
+//      when fewer than K others are larger; more, in heavily tied rows: the K-th largest
+//      from a most-significant-bit-first search) and writes their blocks in ascending
+//      order, then the local block.
+constexpr int kRowThreads = 256;
+constexpr int kRowPer = 32;
+constexpr int kRowMax = kRowThreads * kRowPer;  // longest row this kernel takes
+
+__global__ __launch_bounds__(kRowThreads) void block_topk_row_kernel(
+    const float* __restrict__ scores, int32_t* __restrict__ out, int G, int nblk, int top_k,
+    int decode, int64_t q_begin, const int32_t* __restrict__ seq_lens, int64_t max_len) {
+  __shared__ uint32_t tmax_s[kRowThreads];
+  __shared__ uint64_t cand[kRowMax];
+  __shared__ int32_t sel_s[64];
+  __shared__ int ncand;
+  __shared__ uint32_t lb_s;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  int b;
+  if (decode) {
+    int64_t L = seq_lens[row / G];
+    L = L < 1 ? 1 : (L > max_len ? max_len : L);
+    b = (int)((L - 1) / kBlock);
+  } else {
+    b = (int)((q_begin + row / G) / kBlock);
+  }
+  int32_t* o = out + row * top_k;
+  if (b + 1 <= top_k) {  // every visible block fits
+    if (tid < top_k) o[tid] = tid <= b ? tid : -1;
+    return;
+  }
+  const int K = top_k - 1;
+  if (tid == 0) o[K] = b;  // the local block is the largest kept id
+  if (K == 0) return;
+  const float* s = scores + row * (int64_t)nblk;
+  uint32_t key[kRowPer];
+  uint32_t tmax = 0;  // below the key of every finite float
+  // key j of this thread is block blk(j): 16-byte loads (4 consecutive blocks) when rows
+  // start 16-byte aligned, else single blocks
+  const bool vec = (nblk & 3) == 0;
+  auto blk = [&](int j) {
+    return vec ? 4 * tid + kRowThreads * 4 * (j >> 2) + (j & 3) : tid + kRowThreads * j;
+  };
+  if (vec) {
+#pragma unroll
+    for (int j4 = 0; j4 < kRowPer / 4; ++j4) {
+      const int c0 = 4 * tid + kRowThreads * 4 * j4;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 < b) f = *reinterpret_cast<const float4*>(s + c0);
+      key[4 * j4 + 0] = c0 + 0 < b ? ordered_key(f.x) : 0u;
+      key[4 * j4 + 1] = c0 + 1 < b ? ordered_key(f.y) : 0u;
+      key[4 * j4 + 2] = c0 + 2 < b ? ordered_key(f.z) : 0u;
+      key[4 * j4 + 3] = c0 + 3 < b ? ordered_key(f.w) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const int c = tid + kRowThreads * j;
+      key[j] = c < b ? ordered_key(s[c]) : 0u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRowPer; ++j) tmax = max(tmax, key[j]);
+  tmax_s[tid] = tmax;
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t v[kRowThreads / 64];
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) v[i] = tmax_s[lane + 64 * i];
+    uint32_t lb = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = lb | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kRowThreads / 64; ++i) cnt += __popcll(__ballot(v[i] >= c));
+      if (cnt >= K) lb = c;
+    }
+    if (lane == 0) lb_s = lb;
+  }
+  __syncthreads();
+  // b > K valid blocks sit in at least K threads, so LB > 0 and padding keys never pass.
+  const uint32_t lb = lb_s;
+#pragma unroll
+  for (int j = 0; j < kRowPer; ++j) {
+    const bool take = key[j] >= lb;
+    const uint64_t m = __ballot(take);
+    if (m == 0) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&ncand, __popcll(m));
+    base = __shfl(base, 0, 64);
+    if (take)
+      cand[base + __popcll(m & lanemask_lt(lane))] =
+          ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk(j));
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int n = ncand;
+  uint64_t tau = 0;
+  constexpr int kHeld = 4;
+  if (n <= 64 * kHeld) {
+    // few candidates: each is kept when fewer than K others are larger (values are distinct)
+    uint64_t v[kHeld];
+    int above[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      v[i] = lane + 64 * i < n ? cand[lane + 64 * i] : 0ull;
+      above[i] = 0;
+    }
+    for (int j = 0; j < n; ++j) {
+      const uint64_t x = cand[j];
+#pragma unroll
+      for (int i = 0; i < kHeld; ++i) above[i] += x > v[i] ? 1 : 0;
+    }
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      const bool kept = lane + 64 * i < n && above[i] < K;
+      const uint64_t m = __ballot(kept);
+      if (kept) sel_s[base + __popcll(m & lanemask_lt(lane))] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[i]);
+      base += __popcll(m);
+    }
+  } else {  // heavily tied rows: a most-significant-bit-first search, counting over LDS
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t c = tau | (1ull << bit);
+      int cnt = 0;
+      for (int i0 = 0; i0 < n; i0 += 64) cnt += __popcll(__ballot(i0 + lane < n && cand[i0 + lane] >= c));
+      if (cnt >= K) tau = c;
+    }
+    int base = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const uint64_t v = i0 + lane < n ? cand[i0 + lane] : 0ull;
+      const bool kept = v >= tau && v != 0ull;
+      const uint64_t m = __ballot(kept);
+      if (kept) sel_s[base + __popcll(m & lanemask_lt(lane))] = (int32_t)(0xFFFFFFFFu - (uint32_t)v);
+      base += __popcll(m);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the K kept blocks in ascending order: each lane ranks one of them among the others
+  if (lane < K) {
+    const int c = sel_s[lane];
+    int rank = 0;
+    for (int i = 0; i < K; ++i) rank += sel_s[i] < c ? 1 : 0;
+    o[rank] = c;
+  }
+}
+
 hipError_t launch_block_topk(const float* block_scores, int32_t* block_idx, int64_t rows, int G,
                              int nblk, int top_k, int decode, int64_t q_begin,
                              const int32_t* seq_lens, int64_t max_len, hipStream_t stream) {
+  if (decode && nblk <= kRowMax) {
+    hipLaunchKernelGGL(block_topk_row_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream,
+                       block_scores, block_idx, G, nblk, top_k, decode, q_begin, seq_lens, max_len);
+    return hipGetLastError();
+  }
   if (nblk > 2048 && rows <= 8192) {
     hipLaunchKernelGGL(block_topk_long_kernel, dim3((unsigned)rows), dim3(64 * kLongWaves), 0,
                        stream, block_scores, block_idx, G, nblk, top_k, decode, q_begin, seq_lens,

@@ -306,12 +306,13 @@ def test_topk_handles_ties_and_minus_zero_on_device():
         assert got[r, 0].tolist() == sel.tolist(), r
 
 
-def test_topk_long_rows_decode():
-    """Decode rows with more than 2048 blocks take the workgroup-per-row selection:
-    random scores, exact ties, -0.0/+0.0, an all-equal row (candidate overflow) and a
-    row whose last segment is shorter than top_k."""
+@pytest.mark.parametrize("nblk_max", [5000, 9000])
+def test_topk_long_rows_decode(nblk_max):
+    """Decode rows take a workgroup per row (rows up to 8192 blocks held in registers;
+    longer rows the segmented selection): random scores, exact ties, -0.0/+0.0, an
+    all-equal row (every block a candidate) and a row whose winners sit in a short tail."""
     G, top_k = 2, 16
-    max_len = 128 * 5000
+    max_len = 128 * nblk_max
     lens = [max_len, 300000, 128 * 2049 + 5]
     nblk = (max_len + 127) // 128
     gen = torch.Generator().manual_seed(5)
