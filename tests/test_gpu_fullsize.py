@@ -66,3 +66,52 @@ def test_prefill_128k_sampled_rows():
                                     q_begin=int(rows[0]), out_offset=int(rows[0]),
                                     label=f"rows {lo}")
         print(lo, info, flush=True)
+
+
+def test_index_kl_128k_sampled_rows():
+    """Index-branch KL loss and gradients at 131072 tokens on the fused index branch's own
+    selection (the launch bench.py times), standalone and with the attention's lse:
+    sampled rows' loss and dq_idx against the oracle (on the oracle's selection, which
+    must agree), and dk_idx through identities that hold at any size."""
+    T, G, Hpg, k = 131072, 8, 8, 16
+    scale = 1.0 / 128 ** 0.5
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=1000 + T,
+                             planted_per_group=8, device="cuda")
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                    index_dim=128, top_k=k, seq_len=T, q_begin=0, q_count=T)
+    idx = msa.alloc_block_idx(p)
+    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
+    lse = torch.empty((T, G * Hpg), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(p, x["q"], x["k"], x["v"], idx, torch.empty_like(x["q"]),
+                                msa.alloc_workspace(p, "sparse_attn_prefill"), lse=lse)
+    loss, dq, dk = msa.index_kl(x, idx, k, scale)
+    loss2, dq2, dk2 = msa.index_kl(x, idx, k, scale, main_lse=lse)
+    torch.cuda.synchronize()
+    print("kl 128k ran", flush=True)
+    # gradient identities (fp64 on the device): row score gradients sum to zero over each
+    # row's keys; and the loss depends on q_idx, k_idx only through their dot products
+    for d_k, d_q, label in ((dk, dq, "standalone"), (dk2, dq2, "main lse")):
+        d64 = d_k.double()
+        zero_rel = float(d64.sum(0).abs().max() / d64.abs().sum(0).max())
+        lhs = float((d64 * x["k_idx"].double()).sum())
+        rhs = float((d_q.double() * x["q_idx"].double()).sum())
+        assert zero_rel < 1e-4, (label, zero_rel)
+        assert abs(lhs - rhs) <= 1e-4 * max(abs(lhs), abs(rhs)), (label, lhs, rhs)
+    assert float((loss - loss2).abs().max()) <= 1e-4 * (1.0 + float(loss.abs().max()))
+    host = {kk: x[kk].cpu() for kk in ("q", "k", "v", "q_idx", "k_idx")}
+    for lo in (2048 + 5, 65536 - 8, T - 16):
+        rows = np.arange(lo, lo + 16)
+        res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], k,
+                          rows=rows)
+        gidx = idx[lo:lo + 16].cpu().numpy()
+        differ = parity.check_selection(gidx, res["sel"], res["near_tie"], k, label=f"rows {lo}")
+        ref = orc.index_kl(host["q"], host["k"], host["q_idx"], host["k_idx"],
+                           orc.selection_array(res["sel"], k), scale, q_begin=lo)
+        keep = np.array([not any((i, g) in differ for g in range(G)) for i in range(16)])
+        sub = {kk: (v[keep] if kk in ("loss", "dq_idx", "dq_abs", "mass_abs", "loss_abs") else v)
+               for kk, v in ref.items()}
+        for lo_l, lo_q, label in ((loss, dq, "standalone"), (loss2, dq2, "main lse")):
+            got_l = parity.np32(lo_l[lo:lo + 16])[keep]
+            got_q = parity.np32(lo_q[lo:lo + 16])[keep]
+            print(lo, label, parity.check_kl(got_l, got_q, sub, np.arange(int(keep.sum())),
+                                             label=f"rows {lo} {label}"), flush=True)
