@@ -546,23 +546,6 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
 }
 
 
-// O^T += V^T . P^T over one 64-key half of the block (bf16): chunk u of the half holds keys
-// 64 * half + 16 u + {4q .. 4q+3, 8 + 4q .. 8 + 4q + 3}, the keys of its P^T registers.
-__device__ __forceinline__ void pv_half_bf16(f32x16* o, const u32x4* pb, const uint16_t* vt,
-                                             int lane, int half) {
-  const int m = lane & 31, q = lane >> 5;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vr = vt + (32 * dt + m) * kVRow + 64 * half + 16 * u + 4 * q;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-      o[dt] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[u], o[dt]);
-    }
-  }
-}
-
 // ---- reverse-index tile attention, bf16 ----------------------------------------------------
 // K and V of each run's block are staged row-major by direct global->LDS loads into one
 // 64 KB buffer, so two workgroups share a CU and one's staging and query gathers overlap
@@ -736,40 +719,6 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
   }
 }
 
-// V^T staging alone (bf16): consecutive lanes take consecutive key pairs of a column chunk.
-template <int NT>
-struct VStage {
-  static constexpr int kItems = (kBlock / 2) * (kHeadDim / 8) / NT;
-  u32x4 vr[2 * kItems];
-  __device__ __forceinline__ void load(const uint16_t* V, int g, int c, int64_t seq_len, int tid) {
-    const int64_t key0 = (int64_t)c * kBlock;
-    const int nk = (int)min((int64_t)kBlock, seq_len - key0);
-    const uint16_t* vg = V + ((int64_t)g * seq_len + key0) * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int it = tid + NT * i;
-      const int r = 2 * (it % (kBlock / 2));
-      const int col = (it / (kBlock / 2)) * 8;
-      vr[2 * i] = r < nk ? *reinterpret_cast<const u32x4*>(vg + r * kHeadDim + col) : u32x4{0u, 0u, 0u, 0u};
-      vr[2 * i + 1] = r + 1 < nk ? *reinterpret_cast<const u32x4*>(vg + (r + 1) * kHeadDim + col)
-                                 : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* Vt, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int it = tid + NT * i;
-      const int r = 2 * (it % (kBlock / 2));
-      const int col = (it / (kBlock / 2)) * 8;
-      const u32x4 a = vr[2 * i], b = vr[2 * i + 1];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<uint32_t*>(&Vt[(col + 2 * j) * kVRow + r]) = (a[j] & 0xffffu) | (b[j] << 16);
-        *reinterpret_cast<uint32_t*>(&Vt[(col + 2 * j + 1) * kVRow + r]) = (a[j] >> 16) | (b[j] & 0xffff0000u);
-      }
-    }
-  }
-};
 
 // ---- query-tile attention over the shared blocks, folding in the rare partials ------------
 // One workgroup (8 waves) per (query tile, group); wave w owns row tile w.

@@ -31,9 +31,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
-}
 // 2^x with the hardware v_exp_f32 (2^-inf = 0; results below 2^-126 flush to 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -50,12 +47,6 @@ struct F32 {
   static constexpr bool is_bf16 = false;
 };
 
-__device__ __forceinline__ float load_elem(const uint16_t* p) { return bf16_bits_to_f32(*p); }
-__device__ __forceinline__ float load_elem(const float* p) { return *p; }
-__device__ __forceinline__ void store_elem(uint16_t* p, float x) {
-  *p = (uint16_t)f32_to_bf16_bits(x);
-}
-__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
 
 // ---- MFMA wrappers --------------------------------------------------------------------
 // 32x32 output tile. Lane l holds column l % 32 and rows 8*(r/4) + 4*(l/32) + r%4, r < 16.
@@ -83,7 +74,6 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ float wave_max_xor(float x, int from_mask) {
   // Max over lanes that differ only in bits >= from_mask (from_mask a power of two).
@@ -92,10 +82,6 @@ __device__ __forceinline__ float wave_max_xor(float x, int from_mask) {
 }
 __device__ __forceinline__ float wave_sum_xor(float x, int from_mask) {
   for (int m = from_mask; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-__device__ __forceinline__ int wave_sum_int(int x) {
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
 
