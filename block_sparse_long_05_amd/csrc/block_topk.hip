@@ -116,6 +116,7 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
     int64_t max_len) {
   __shared__ uint32_t cand_key[kTopkWaves][kCandCap];
   __shared__ int32_t cand_idx[kTopkWaves][kCandCap];
+  __shared__ int32_t kept_w[kTopkWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kTopkWaves + wave;
@@ -137,6 +138,87 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
   if (lane == 0) o[K] = b;  // the local block is the largest kept id
   if (K == 0) return;
   const float* s = scores + row * (int64_t)nblk;
+  uint32_t* ck = cand_key[wave];
+  int32_t* ci = cand_idx[wave];
+
+  // Rows of up to 2048 blocks: the row is read once into registers (16-byte loads when
+  // rows start 16-byte aligned), all loads in flight together; the candidates >= LB are
+  // ranked as distinct 64-bit values (key << 32) | ~block, which encode the tie rule, so
+  // their order in LDS does not matter.
+  constexpr int kWaveHeld = 32;
+  if (b <= 64 * kWaveHeld) {
+    uint32_t key[kWaveHeld];
+    const bool vec = (nblk & 3) == 0;
+    auto blk = [&](int j) { return vec ? 4 * lane + 256 * (j >> 2) + (j & 3) : lane + 64 * j; };
+    if (vec) {
+#pragma unroll
+      for (int j4 = 0; j4 < kWaveHeld / 4; ++j4) {
+        const int c0 = 4 * lane + 256 * j4;
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c0 < b) f = *reinterpret_cast<const float4*>(s + c0);
+        key[4 * j4 + 0] = c0 + 0 < b ? ordered_key(f.x) : 0u;
+        key[4 * j4 + 1] = c0 + 1 < b ? ordered_key(f.y) : 0u;
+        key[4 * j4 + 2] = c0 + 2 < b ? ordered_key(f.z) : 0u;
+        key[4 * j4 + 3] = c0 + 3 < b ? ordered_key(f.w) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kWaveHeld; ++j) {
+        const int c = lane + 64 * j;
+        key[j] = c < b ? ordered_key(s[c]) : 0u;
+      }
+    }
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int j = 0; j < kWaveHeld; ++j) lmax = max(lmax, key[j]);
+    uint32_t lb = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = lb | (1u << bit);
+      if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
+    }
+    // b > K valid blocks sit in at least K lanes, so LB > 0 and padding keys never pass
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kWaveHeld; ++j) {
+      const bool take = key[j] >= lb;
+      const uint64_t m = __ballot(take);
+      const int pos = n + __popcll(m & lanemask_lt(lane));
+      if (take && pos < kCandCap) {
+        ck[pos] = key[j];
+        ci[pos] = blk(j);
+      }
+      n += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (n <= kCandCap) {
+      int base = 0;
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const bool valid = i0 + lane < n;
+        const uint64_t v =
+            valid ? ((uint64_t)ck[i0 + lane] << 32) | (0xFFFFFFFFu - (uint32_t)ci[i0 + lane]) : 0ull;
+        int above = 0;
+        for (int jj = 0; jj < n; ++jj)
+          above += (((uint64_t)ck[jj] << 32) | (0xFFFFFFFFu - (uint32_t)ci[jj])) > v ? 1 : 0;
+        const bool kept = valid && above < K;
+        const uint64_t m = __ballot(kept);
+        if (kept) kept_w[wave][base + __popcll(m & lanemask_lt(lane))] = ci[i0 + lane];
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < K) {  // ascending block order: each lane ranks one kept block
+        const int c = kept_w[wave][lane];
+        int rank = 0;
+        for (int i = 0; i < K; ++i) rank += kept_w[wave][i] < c ? 1 : 0;
+        o[rank] = c;
+      }
+      return;
+    }
+    // more candidates than LDS holds (heavily tied rows): the general path below
+  }
 
   // 1. lower bound from the lane maxima.
   uint32_t lmax = 0;  // below the key of every finite float
@@ -147,8 +229,6 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
     if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
   }
   // 2. compact the candidates (ascending block order).
-  uint32_t* ck = cand_key[wave];
-  int32_t* ci = cand_idx[wave];
   int n = 0;
   for (int c0 = 0; c0 < b; c0 += 64) {
     const int c = c0 + lane;
