@@ -218,6 +218,14 @@ def run_prefill(name, cfg, args, torch, msa, synth):
                          index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n,
                          algo=args.algo) for c0, n in chunks]
     fused = args.index == "fused" and all(msa.index_topk_supported(p) for p in probs)
+    # the fused index branch needs no workspace, so it can take more rows per launch than
+    # the attention (default: the whole sequence in one launch, one tail instead of one
+    # per chunk)
+    ichunk = min(args.index_chunk or T, T) if fused else chunk
+    ichunks = [(c0, min(ichunk, T - c0)) for c0 in range(0, T, ichunk)]
+    iprobs = [msa.Problem(dtype=cfg["dtype"], mode="prefill", num_groups=G, heads_per_group=Hpg,
+                          index_dim=d_idx, top_k=top_k, seq_len=T, q_begin=c0, q_count=n)
+              for c0, n in ichunks] if fused else None
     bs = None if fused else torch.empty((chunk, G, probs[0].nblk), dtype=torch.float32,
                                         device="cuda")
     idx_full = torch.empty((T, G, top_k), dtype=torch.int32, device="cuda")
@@ -227,20 +235,22 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     timers = {}
 
     def step(timed):
+        if fused:
+            for p, (c0, n) in zip(iprobs, ichunks):
+                if timed:
+                    with timers.setdefault("index_topk", KernelTimer(torch)):
+                        msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx_full[c0:c0 + n])
+                else:
+                    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx_full[c0:c0 + n])
         for p, (c0, n) in zip(probs, chunks):
             idx = idx_full[c0:c0 + n]
             if not timed:
-                if fused:
-                    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
-                else:
+                if not fused:
                     msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
                     msa.msa_block_topk(p, bs, idx)
                 msa.msa_sparse_attn_prefill(p, q, x["k"], x["v"], idx, out, ws)
                 continue
-            if fused:
-                with timers.setdefault("index_topk", KernelTimer(torch)):
-                    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
-            else:
+            if not fused:
                 with timers.setdefault("index_scores", KernelTimer(torch)):
                     msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
                 with timers.setdefault("block_topk", KernelTimer(torch)):
@@ -266,18 +276,21 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
-    per_kernel = {k: v.mean_ms() * len(chunks) for k, v in timers.items()}
+    per_kernel = {k: v.mean_ms() * (len(ichunks) if k == "index_topk" else len(chunks))
+                  for k, v in timers.items()}
 
     idx_flops = prefill_index_flops(T, G, d_idx, top_k)
     att_flops = prefill_attn_flops(T, G * Hpg, 128, top_k)
     peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
     idx_name = "index_topk" if fused else "index_scores"
     idx_ms_launch = timers[idx_name].mean_ms()
-    idx_tflops = idx_flops / len(chunks) / (idx_ms_launch * 1e-3) / 1e12
+    n_idx_launch = len(ichunks) if fused else len(chunks)
+    idx_tflops = idx_flops / n_idx_launch / (idx_ms_launch * 1e-3) / 1e12
     total_tflops = (idx_flops + att_flops) / (ms * 1e-3) / 1e12
     res = dict(
         workload=name, T=T, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
-        chunk=chunk, algo=args.algo, index_branch="fused" if fused else "separate",
+        chunk=chunk, index_launch_rows=ichunk, algo=args.algo,
+        index_branch="fused" if fused else "separate",
         ms_per_step=ms, wall_s=wall, tok_per_s=T / (ms * 1e-3),
         kernel_ms_per_step=per_kernel,
         flops=dict(index=idx_flops, attention=att_flops),
@@ -287,7 +300,7 @@ def run_prefill(name, cfg, args, torch, msa, synth):
                       achieved=idx_tflops, peak=peak, unit="TFLOP/s", frac=idx_tflops / peak,
                       traffic=measured_traffic("index_topk_prefill" if fused
                                                else "index_scores_prefill"),
-                      work_per_launch=idx_flops / len(chunks), launch_ms=idx_ms_launch),
+                      work_per_launch=idx_flops / n_idx_launch, launch_ms=idx_ms_launch),
     )
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
         f"path {total_tflops:.1f} TFLOP/s ({res['path_frac_of_peak']*100:.1f}% of peak)  "
@@ -591,6 +604,8 @@ def main():
                          "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="prefill query rows per call (0 = the workload's default)")
+    ap.add_argument("--index-chunk", type=int, default=0,
+                    help="query rows per fused index launch (0: the whole sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kl", type=int, default=1,
                     help="also time the index-branch KL loss + gradients on the prefill's "

@@ -162,6 +162,8 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(int64_t nb, int32_t* __re
   const int64_t per = (nb + 1023) / 1024;
   const int64_t lo = min(nb, tid * per), hi = min(nb, lo + per);
   int32_t s = 0;
+  // unrolled so that several loads of the thread's range are in flight at once
+#pragma unroll 8
   for (int64_t k = lo; k < hi; ++k) s += bucket_off[k];
   part[tid] = s;
   __syncthreads();
@@ -172,6 +174,7 @@ __global__ __launch_bounds__(1024) void kv_scan_kernel(int64_t nb, int32_t* __re
     __syncthreads();
   }
   int32_t run = part[tid] - s;  // exclusive prefix of this thread's range
+#pragma unroll 8
   for (int64_t k = lo; k < hi; ++k) {
     const int32_t c = bucket_off[k];
     bucket_off[k] = run;
