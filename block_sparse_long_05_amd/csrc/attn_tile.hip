@@ -87,7 +87,8 @@ __device__ __forceinline__ int64_t entry_bucket(const int32_t* block_idx, int64_
 // One wave per (query tile, group): a block is shared when at least half of the tile's
 // tokens keep it. Candidates are the blocks of the tile's last token (any block kept by
 // half of the tokens is likely among them; the split only moves work between the two
-// paths, every kept entry is still handled exactly once).
+// paths, every kept entry is still handled exactly once). The tile's ids are read once,
+// 64 at a time, and each candidate's count comes from one ballot per 64 ids.
 __global__ __launch_bounds__(256) void kv_classify_kernel(const int32_t* __restrict__ block_idx,
                                                           int32_t* __restrict__ shared, int G,
                                                           int top_k, int64_t q_begin,
@@ -105,13 +106,21 @@ __global__ __launch_bounds__(256) void kv_classify_kernel(const int32_t* __restr
     cand = block_idx[((i0 + ntok - 1) * G + g) * top_k + lane];
     if (cand < 0 || (int64_t)cand > t_last / kBlock) cand = -1;
   }
-  int cnt = 0;
-  for (int tok = 0; tok < ntok; ++tok) {
-    const int32_t* tl = block_idx + ((i0 + tok) * G + g) * top_k;
-    const int b = (int)((q_begin + i0 + tok) / kBlock);
-    for (int s = 0; s < top_k; ++s) {
-      const int c = tl[s];
-      cnt += (c >= 0 && c == cand && c <= b) ? 1 : 0;
+  int cnt = 0;  // lane j: how many of the tile's visible ids equal candidate j
+  const int ne = ntok * top_k;
+  for (int e0 = 0; e0 < ne; e0 += 64) {
+    const int e = e0 + lane;
+    int c = -1;
+    if (e < ne) {
+      const int tok = e / top_k;
+      c = block_idx[((i0 + tok) * G + g) * top_k + (e - tok * top_k)];
+      if ((int64_t)c > (q_begin + i0 + tok) / kBlock) c = -1;
+    }
+    for (int j = 0; j < top_k; ++j) {
+      const int cj = __builtin_amdgcn_readlane(cand, j);
+      if (cj < 0) continue;
+      const int m = __popcll(__ballot(c == cj));
+      cnt += lane == j ? m : 0;
     }
   }
   const bool keep = cand >= 0 && 2 * cnt >= ntok;
