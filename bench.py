@@ -661,7 +661,7 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": hib, "scaling": "weak",
-        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic (seeded; see DESIGN.md)",
+        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic: seeded N(0,1) inputs with planted index blocks",
         "config": config, "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
     }
