@@ -285,7 +285,8 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
 // One wave per (sequence, head). Lanes hold the (m, l) of 64 splits at a time (all
 // loaded at once): pass 1 reduces the global max, pass 2 forms each split's weight in
 // its lane and broadcasts it while every lane streams its two dims of the partials,
-// 8 splits in flight. The order of the sum is fixed, so the result is deterministic.
+// 8 splits in flight (up to 32 splits: all partials requested up front instead). The
+// order of the sum is fixed, so the result is deterministic.
 template <class E>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml,
@@ -295,6 +296,33 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   const int64_t bg = blockIdx.x / Hpg;
   const int h = blockIdx.x % Hpg;
   const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  constexpr int kFew = 32;
+  if (nsplit <= kFew) {
+    // up to 32 splits (top_k <= 16): every partial and every (m, l) is requested at once,
+    // so the wave waits for memory once
+    float2 o[kFew];
+#pragma unroll
+    for (int k = 0; k < kFew; ++k)
+      o[k] = k < nsplit ? *reinterpret_cast<const float2*>(
+                              part_o + ((bg * nsplit + k) * Hpg + h) * kHeadDim + 2 * lane)
+                        : make_float2(0.f, 0.f);
+    const float2 v = lane < nsplit ? ml[(bg * nsplit + lane) * Hpg + h] : make_float2(-INFINITY, 0.f);
+    const float Mf = wave_max_xor(v.x, 1);
+    const float w = v.x == -INFINITY ? 0.f : fast_exp2(v.x - Mf);
+    const float Lf = wave_sum_xor(w * v.y, 1);
+    float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kFew; ++k) {
+      if (k < nsplit) {
+        const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+        b0 += wk * o[k].x;
+        b1 += wk * o[k].y;
+      }
+    }
+    const float invf = Lf > 0.f ? 1.f / Lf : 0.f;
+    KOp<E>::store2(out + (bg * Hpg + h) * kHeadDim + 2 * lane, b0 * invf, b1 * invf);
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < nsplit; s0 += 64) {
     const int sp = s0 + lane;
