@@ -156,9 +156,13 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
     if constexpr (kPreV) {
       if (kspan == 64) {
         const elem* vp0 = vblk + 2 * lane;
+        // unconditional loads (rows past the valid keys read row 0, then zeroed), so that
+        // no load sits behind a branch and waits alone
 #pragma unroll
-        for (int j = 0; j < 64; ++j)
-          vpre[j] = j < nvalid ? *reinterpret_cast<const uint32_t*>(vp0 + (int64_t)j * kHeadDim) : 0u;
+        for (int j = 0; j < 64; ++j) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vp0 + (int64_t)(j < nvalid ? j : 0) * kHeadDim);
+          vpre[j] = j < nvalid ? w : 0u;
+        }
       }
     }
     // S^T = K . Q^T for the 16-key tiles (8 per block, 4 per half block).
@@ -172,7 +176,10 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
         const bool ok = kk < nvalid;
         const elem* kp = kblk + (ok ? kk : 0) * kHeadDim + kgrp * E::kPerLane;
 #pragma unroll
-        for (int s = 0; s < kNStep; ++s) a = mfma16(ok ? O::load(kp + s * O::kStep) : O::zero(), qop[s], a);
+        for (int s = 0; s < kNStep; ++s) {
+          const typename O::type w = O::load(kp + s * O::kStep);
+          a = mfma16(ok ? w : O::zero(), qop[s], a);
+        }
       }
       s4[kt] = a;
     }
