@@ -3,7 +3,8 @@ times, on outputs the oracle can compute one by one (sampled query rows / sequen
 
 Workloads: decode of 4 sequences x 131072 cached tokens (all rows checked), decode of
 8 x 1,048,576 (two sequences checked), causal prefill of 131072 tokens (sampled
-32-token slices). All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
+32-token slices) and of 1,048,576 tokens (sampled 8-token slices), the index-branch KL
+loss at 131072 tokens. All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
 index dim 128, 128-token blocks, top_k 16, planted blocks as in the benchmark.
 """
 
@@ -115,3 +116,37 @@ def test_index_kl_128k_sampled_rows():
             got_q = parity.np32(lo_q[lo:lo + 16])[keep]
             print(lo, label, parity.check_kl(got_l, got_q, sub, np.arange(int(keep.sum())),
                                              label=f"rows {lo} {label}"), flush=True)
+
+
+def test_prefill_1m_sampled_rows():
+    """Causal prefill of 1,048,576 tokens as the benchmark runs it (the fused index branch over
+    all rows in one launch, the attention in chunks of 131072 rows sharing one workspace):
+    sampled query rows against the oracle."""
+    T, G, Hpg, k, chunk = 1 << 20, 8, 8, 16, 131072
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=1000 + T,
+                             planted_per_group=16, device="cuda")
+    p_all = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                        index_dim=128, top_k=k, seq_len=T, q_begin=0, q_count=T)
+    idx = msa.alloc_block_idx(p_all)
+    msa.msa_index_topk(p_all, x["q_idx"], x["k_idx"], idx)
+    out = torch.empty_like(x["q"])
+    probs = [msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                         index_dim=128, top_k=k, seq_len=T, q_begin=c0, q_count=chunk)
+             for c0 in range(0, T, chunk)]
+    ws = msa.alloc_workspace(probs[-1], "sparse_attn_prefill")
+    for p in probs:
+        msa.msa_sparse_attn_prefill(p, x["q"], x["k"], x["v"], idx[p.q_begin:p.q_begin + chunk],
+                                    out, ws)
+    torch.cuda.synchronize()
+    print("prefill 1M ran", flush=True)
+    del ws
+    host = {kk: x[kk].cpu() for kk in ("q", "k", "v", "q_idx", "k_idx")}
+    for lo in (chunk - 4, 600000, T - 8):
+        rows = np.arange(lo, lo + 8)
+        res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], k,
+                          rows=rows)
+        got_out = out[lo:lo + 8].float().cpu().numpy()
+        got_idx = idx[lo:lo + 8].cpu().numpy()
+        info = parity.check_prefill(host, rows, got_out, got_idx, None, res, k, q_begin=lo,
+                                    out_offset=lo, label=f"1M rows {lo}")
+        print(lo, info, flush=True)
