@@ -46,6 +46,8 @@ CASES = [
     (2100, 8, 8, 16, 4, 1.0 / math.sqrt(128), 2),   # 16 blocks x 128 tokens, 8 x 8 heads
     (100, 1, 1, 1, 0, 0.05, 3),                      # one partial block
     (1333, 4, 2, 6, 2, 0.3, 4),
+    (600, 1, 16, 3, 1, 0.3, 5),                      # 16 heads per group (the maximum)
+    (1500, 2, 4, 24, 2, 0.15, 6),                    # top_k 24 > blocks: padded rows
 ]
 
 
