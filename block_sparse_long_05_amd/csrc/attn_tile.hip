@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
       float p[4][16];
       float mx = -INFINITY;
       // 32-bit limit, clamped to [-1, 128], with the lane's key offset 4q folded in
-      const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
+      const int lim = min(max((int)t - c * kBlock, -1), kBlock);
       const int limq = lim - 4 * q;
       const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
 #pragma unroll
@@ -626,8 +626,9 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
     // across it (the empty asm hides that the lane id does not change).
     int tid_v = tid;
     asm volatile("" : "+v"(tid_v));
-    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
-    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    k_block_dma_s<256>(K, g, c, seq_len, Kb, wv, dma_lane_off<false>(tid_v & 63), tid_v);
+    k_block_dma_s<256, true>(V, g, c, seq_len, Vb, wv, dma_lane_off<true>(tid_v & 63), tid_v);
     const int nrt = (r1 - r0 + epr - 1) / epr;
     auto row_of = [&](int rt, int32_t& id, int64_t& t) {
       const int ent = r0 + rt * epr + e;
@@ -650,8 +651,9 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       int lane_v = lane;
       asm volatile("" : "+v"(lane_v));
       const int n32v = lane_v & 31, qv = lane_v >> 5;
-      const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
-      const int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
+      const int lim = min(max((int)t - c * kBlock, -1), kBlock);
+      int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
+      asm volatile("" : "+v"(limq));
       const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
       const int32_t cur_id = id;
       const bool cur_ok = ok;
@@ -665,13 +667,17 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
         for (int kk2 = 0; kk2 < 2; ++kk2) {
           const int kt = 2 * half + kk2;
           const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+          // the compare and select only where a row of the wave ends inside the block
+          if (masked) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = sv[r];
-            if (masked) x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
-            p[kk2][r] = x;
-            mx = fmaxf(mx, x);
+            for (int r = 0; r < 16; ++r)
+              p[kk2][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[kk2][r] = sv[r];
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kk2][r]);
         }
         if (half == 1 && rt + 4 < nrt) {  // S^T is done with this row tile's queries
           ok = row_of(rt + 4, id, t);
@@ -818,7 +824,7 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
       typename T::qop_t qop[T::kQSteps];
       T::load_q(qop, Q + (t_r[rt] * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, sel);
       const int lim =
-          (int)min<int64_t>(max<int64_t>(t_r[rt] - (int64_t)c * kBlock, -1), kBlock);
+          min(max((int)t_r[rt] - c * kBlock, -1), kBlock);
       const int limq = lim - 4 * q;
       const bool causal = __ballot(sel && lim < kBlock - 1) != 0;
       float p[4][16];
@@ -963,8 +969,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   __shared__ __align__(16) uint8_t Vb0[kBlock * 256];
   __shared__ __align__(16) uint8_t Vb1[kBlock * 256];
   __shared__ int32_t sl[64];
-  __shared__ uint64_t selmask[256];   // per token: which shared blocks it keeps
-  __shared__ uint64_t raremask[256];  // per token: which slots go through the partials
+  __shared__ unsigned long long selmask[256];   // per token: which shared blocks it keeps
+  __shared__ unsigned long long raremask[256];  // per token: which slots go through the partials
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -975,31 +981,30 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   const int64_t i0 = tile * QT;
   const int ntok = (int)min((int64_t)QT, q_count - i0);
   const int Hq = G * Hpg;
-  if (tid < top_k) sl[tid] = shared[(tile * G + g) * top_k + tid];
+  // the shared list (ascending, -1 padded): each wave counts it from one load per lane
+  const int slv = lane < top_k ? shared[(tile * G + g) * top_k + lane] : -1;
+  const int ns = __popcll(__ballot(slv >= 0));
+  if (tid < 64) sl[tid] = slv;  // -1 past the list
+  if (tid < QT) {
+    selmask[tid] = 0ull;
+    raremask[tid] = 0ull;
+  }
   __syncthreads();
-  int ns = 0;
-  while (ns < top_k && sl[ns] >= 0) ++ns;
-  if (tid < ntok) {
-    const int32_t* tl = block_idx + ((i0 + tid) * G + g) * top_k;
-    const int b = (int)((q_begin + i0 + tid) / kBlock);
-    int cs[KMAX];
+  // Per token: bit j of selmask = it keeps shared block j, bit s of raremask = its slot s
+  // is visible and not shared. One thread per kept entry (coalesced id loads).
+  for (int en = tid; en < ntok * top_k; en += 512) {
+    const int tk = en / top_k;
+    const int s2 = en - tk * top_k;
+    const int c = block_idx[((i0 + tk) * G + g) * top_k + s2];
+    const int b = (int)((q_begin + i0 + tk) / kBlock);
+    if (c < 0 || c > b) continue;
+    int jm = -1;
 #pragma unroll
-    for (int s2 = 0; s2 < KMAX; ++s2) cs[s2] = s2 < top_k ? tl[s2] : -1;  // all loads in flight
-    uint64_t mk = 0, rk = 0;
-#pragma unroll
-    for (int s2 = 0; s2 < KMAX; ++s2) {
-      const int c = cs[s2];
-      if (c < 0 || c > b) continue;
-      bool found = false;
-      for (int j = 0; j < ns; ++j)
-        if (sl[j] == c) {
-          mk |= 1ull << j;
-          found = true;
-        }
-      if (!found) rk |= 1ull << s2;
-    }
-    selmask[tid] = mk;
-    raremask[tid] = rk;
+    for (int j = 0; j < KMAX; ++j) jm = sl[j] == c ? j : jm;  // c >= 0 never meets the -1s
+    if (jm >= 0)
+      atomicOr(&selmask[tk], 1ull << jm);
+    else
+      atomicOr(&raremask[tk], 1ull << s2);
   }
 
   const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
@@ -1010,6 +1015,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   const bool ok = e < epr && tok < ntok;
   const int64_t irow = i0 + (ok ? tok : 0);
   const int64_t t = q_begin + irow;
+  const int tq = (int)t;
   T::qop_t qop[T::kQSteps];
   T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
   __syncthreads();
@@ -1018,10 +1024,11 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4] = {};
 
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   if (ns > 0) {
     const int c0 = __builtin_amdgcn_readfirstlane(sl[0]);
-    k_block_dma<512>(K, g, c0, seq_len, Kb0, tid);
-    k_block_dma<512, true>(V, g, c0, seq_len, Vb0, tid);
+    k_block_dma_s<512>(K, g, c0, seq_len, Kb0, wv, dma_lane_off<false>(lane), tid);
+    k_block_dma_s<512, true>(V, g, c0, seq_len, Vb0, wv, dma_lane_off<true>(lane), tid);
   }
   auto shared_block = [&](int j, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     const int c = __builtin_amdgcn_readfirstlane(sl[j]);  // uniform: scalar staging base
@@ -1037,14 +1044,20 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const int n32v = lane_v & 31, qv = lane_v >> 5;
     if (j + 1 < ns) {
       const int cn = __builtin_amdgcn_readfirstlane(sl[j + 1]);
-      k_block_dma<512>(K, g, cn, seq_len, Kn, tid_v);
-      k_block_dma<512, true>(V, g, cn, seq_len, Vn, tid_v);
+      k_block_dma_s<512>(K, g, cn, seq_len, Kn, wv, dma_lane_off<false>(lane_v), tid_v);
+      k_block_dma_s<512, true>(V, g, cn, seq_len, Vn, wv, dma_lane_off<true>(lane_v), tid_v);
     }
     const bool sel = (mymask >> j) & 1ull;
     if (__ballot(sel) == 0) return;
-    const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
-    const int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
-    const bool causal = __ballot(sel && lim < kBlock - 1) != 0;
+    // last visible key offset in the block (int32: t < 2^31), -1 when the row did not keep
+    // it; rows without a token (ok false) are never stored and need no mask
+    const int lim = min(max(tq - c * kBlock, -1), kBlock - 1);
+    const int lime = sel ? lim : -1;
+    // one uniform test per block: most shared blocks are fully visible to every row of the
+    // wave, and then the scores go to the softmax without a compare and select each
+    const bool masked = __ballot(ok && lime < kBlock - 1) != 0;
+    int limq = lime - 4 * qv;  // the lane's key offset 4q folded into the limit
+    asm volatile("" : "+v"(limq));
     // the block's 128 keys in two halves of 64, one online-softmax step each
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1054,15 +1067,16 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const int kt = 2 * half + kk2;
         const f32x16 sv = s_tile_swz(Kc, 32 * kt + n32v, qop, qv);
+        if (masked) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sel ? sv[r] : -INFINITY;
-          if (causal) {
-            x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
-          }
-          p[kk2][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r)
+            p[kk2][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[kk2][r] = sv[r];
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kk2][r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mxs = mx * qk_scale;
@@ -1105,15 +1119,34 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
 
   // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
   // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
-  // them: each load instruction covers whole cache lines).
+  // them: each load instruction covers whole cache lines). Each lane walks only its own
+  // rare slots, in slot order, so a wave iterates as often as its busiest token has rare
+  // slots. The partials are read through buffer views of the tile's entries (group g, 32-bit
+  // offsets); a lane with no slot left reads past the bound and gets zeros, so no load
+  // sits behind a branch.
   float m_fin = m_run;  // the reference maximum of l_run once the partials are in
   if (__ballot(myrare != 0)) {
-    const int64_t prow0 = (irow * G + g) * top_k * Hpg + h;
-    const float2* ml2 = reinterpret_cast<const float2*>(part_ml);
+    const int64_t ebase = (i0 * G + g) * top_k;
+    const uint32_t span = (uint32_t)((int64_t)(ntok - 1) * G * top_k + top_k);  // < 2^20
+    const __amdgpu_buffer_rsrc_t v_ml = buffer_view(part_ml + ebase * Hpg * 2, span * Hpg * 8);
+    const __amdgpu_buffer_rsrc_t v_o =
+        buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
+    const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
     float M = m_run;
+    for (uint64_t rem = myrare; __ballot(rem != 0);) {
+      float x[4];
+      bool hs[4];
 #pragma unroll
-    for (int s2 = 0; s2 < KMAX; ++s2)
-      if ((myrare >> s2) & 1ull) M = fmaxf(M, ml2[prow0 + (int64_t)s2 * Hpg].x);
+      for (int k2 = 0; k2 < 4; ++k2) {
+        hs[k2] = rem != 0;
+        const uint32_t s2 = (uint32_t)__builtin_ctzll(rem | (1ull << 63));
+        rem &= rem - 1ull;
+        const uint32_t off = hs[k2] ? ((tok_e + s2) * Hpg + h) * 8 : kBufNone;
+        x[k2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v_ml, off, 0, 0));
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
+    }
     m_fin = M;
     const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
     l_run *= a;
@@ -1121,27 +1154,39 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][r] *= a;
-#pragma unroll 2
-    for (int s2 = 0; s2 < KMAX; ++s2) {
-      const bool rare = (myrare >> s2) & 1ull;
-      if (!__ballot(rare)) continue;
-      const int64_t prow = prow0 + (int64_t)s2 * Hpg;
-      const float2 ml = rare ? ml2[prow] : make_float2(-INFINITY, 0.f);
-      const uint16_t* src = part_o + (prow - h) * kHeadDim + 8 * (h + Hpg * q);
-      u32x4 w4[8];
+    const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
+    for (uint64_t rem = myrare; __ballot(rem != 0);) {
+      float2 ml[2];
+      u32x4 w4[2][8];
+      bool hs[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w4[i] = rare ? *reinterpret_cast<const u32x4*>(src + i * 16 * Hpg) : u32x4{0u, 0u, 0u, 0u};
-      const float w = rare ? ml.y * fast_exp2(ml.x - M) : 0.f;
-      l_run += w;
+      for (int k2 = 0; k2 < 2; ++k2) {
+        hs[k2] = rem != 0;
+        const uint32_t ent = tok_e + (uint32_t)__builtin_ctzll(rem | (1ull << 63));
+        rem &= rem - 1ull;
+        ml[k2] = __builtin_bit_cast(
+            float2, __builtin_amdgcn_raw_buffer_load_b64(
+                        v_ml, hs[k2] ? (ent * Hpg + h) * 8 : kBufNone, 0, 0));
+        const uint32_t ob = hs[k2] ? ent * Hpg * kHeadDim * 2 + lane_b : kBufNone;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
+          w4[k2][i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_o, ob + i * 32 * Hpg, 0, 0));
+      }
 #pragma unroll
-        for (int k2 = 0; k2 < 8; ++k2) {
-          const uint32_t bits = k2 & 1 ? w4[i][k2 >> 1] >> 16 : w4[i][k2 >> 1] & 0xffffu;
-          const int r = 4 * (2 * (i & 1) + (k2 >> 2)) + (k2 & 3);
-          o[i >> 1][r] = fmaf(w, bf16_bits_to_f32(bits), o[i >> 1][r]);
-        }
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - M) : 0.f;
+        l_run += w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j2 = 0; j2 < 8; ++j2) {
+            const uint32_t bits =
+                j2 & 1 ? w4[k2][i][j2 >> 1] >> 16 : w4[k2][i][j2 >> 1] & 0xffffu;
+            const int r = 4 * (2 * (i & 1) + (j2 >> 2)) + (j2 & 3);
+            o[i >> 1][r] = fmaf(w, bf16_bits_to_f32(bits), o[i >> 1][r]);
+          }
+      }
     }
   }
   if (ok) {
@@ -1200,12 +1245,14 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16_kernel(
     asm volatile("" : "+v"(tid_v));
     const int lane_v = tid_v & 63;
     const int n32v = lane_v & 31, qv = lane_v >> 5;
-    k_block_dma<256>(K, g, c, seq_len, Kb, tid_v);
-    k_block_dma<256, true>(V, g, c, seq_len, Vb, tid_v);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    k_block_dma_s<256>(K, g, c, seq_len, Kb, wv, dma_lane_off<false>(lane_v), tid_v);
+    k_block_dma_s<256, true>(V, g, c, seq_len, Vb, wv, dma_lane_off<true>(lane_v), tid_v);
     MSA_WAIT_VMCNT(0);
     __syncthreads();
-    const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock);
-    const int limq = lim - 4 * q;
+    const int lim = min(max((int)t - c * kBlock, -1), kBlock);
+    int limq = lim - 4 * qv;
+    asm volatile("" : "+v"(limq));
     const bool causal = __ballot(lim < kBlock - 1) != 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1215,13 +1262,17 @@ __global__ __launch_bounds__(256, 2) void dense_attn_bf16_kernel(
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const int kt = 2 * half + kk2;
         const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+        // the compare and select only on the diagonal blocks
+        if (causal) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sv[r];
-          if (causal) x = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? x : -INFINITY;
-          p[kk2][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r)
+            p[kk2][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[kk2][r] = sv[r];
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kk2][r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mxs = mx * qk_scale;

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
       const int64_t rowg = id / top_k;                 // chunk row * G + g
       const int64_t t = q_begin + rowg / G;
       // last visible key offset in the block, folded with the lane's key offset 4q
-      const int lim = (int)min<int64_t>(max<int64_t>(t - (int64_t)c * kBlock, -1), kBlock - 1);
+      const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
       const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
       const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
       u32x4 qiop[kHeadDim / 16];

@@ -31,6 +31,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
+// Buffer views (raw buffer loads: 32-bit byte offsets from a base, bounded by a byte count):
+// word 3 of a gfx9 buffer descriptor selects 32-bit data and raw access; a load at or past
+// the bound returns zeros without touching memory.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufWord3);
+}
+constexpr uint32_t kBufNone = 0x80000000u;  // an offset past every view's bound (< 2^31)
+
 // 2^x with the hardware v_exp_f32 (2^-inf = 0; results below 2^-126 flush to 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

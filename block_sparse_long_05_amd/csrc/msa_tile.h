@@ -37,6 +37,41 @@ __device__ __forceinline__ void k_block_dma(const uint16_t* K, int g, int c, int
   }
 }
 
+// The same staging with the wave-uniform parts of every address in scalar registers.
+// Wave w of NT / 64 loads rows 4 li + lane / 16 for li = w * P + i (P = loads per wave):
+// row offset 256 (4 li) is uniform, and the swizzled chunk of lane (L = lane / 16,
+// x = lane % 16) is x ^ (4 (i % 4) + L) (row swizzle) or x ^ (4 L + i % 4) (V swizzle),
+// so a lane's byte offset within the 1 KiB of load li is dma_lane_off(lane) xor-ed with
+// 64 (i % 4) or 16 (i % 4). `wave` must be wave-uniform. A block that ends before its
+// 128th row (the sequence's last) takes the general path above.
+template <bool kVSwz>
+__device__ __forceinline__ uint32_t dma_lane_off(int lane) {
+  const int L = (lane >> 4) & 3, x = lane & 15;
+  return (uint32_t)(256 * L + 16 * (x ^ (kVSwz ? 4 * L : L)));
+}
+
+template <int NT, bool kVSwz = false>
+__device__ __forceinline__ void k_block_dma_s(const uint16_t* K, int g, int c, int64_t seq_len,
+                                              uint8_t* kbuf, int wave, uint32_t lane_off,
+                                              int tid) {
+  const int64_t key0 = (int64_t)c * kBlock;
+  if (seq_len - key0 < kBlock) {
+    k_block_dma<NT, kVSwz>(K, g, c, seq_len, kbuf, tid);
+    return;
+  }
+  constexpr int kPer = kBlock * 256 / 1024 / (NT / 64);  // 1 KiB loads per wave
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(K + ((int64_t)g * seq_len + key0) * kHeadDim) +
+                        (size_t)wave * kPer * 1024;
+  uint8_t* lds = kbuf + wave * kPer * 1024;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const uint32_t off = lane_off ^ (uint32_t)((kVSwz ? 16 : 64) * (i & 3));
+    __builtin_amdgcn_global_load_lds((const void*)(base + 1024 * i + off),
+                                     (__attribute__((address_space(3))) void*)(lds + 1024 * i),
+                                     16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
   f32x16 acc = {};
 #pragma unroll
