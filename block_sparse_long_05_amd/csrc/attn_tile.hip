@@ -1132,12 +1132,14 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const __amdgpu_buffer_rsrc_t v_o =
         buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
     const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
+    // slots whose loads are issued together: (m, l) pairs in pass 1, partials in pass 2
+    constexpr int kMlPer = 4, kPartPer = 2;
     float M = m_run;
     for (uint64_t rem = myrare; __ballot(rem != 0);) {
-      float x[4];
-      bool hs[4];
+      float x[kMlPer];
+      bool hs[kMlPer];
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
+      for (int k2 = 0; k2 < kMlPer; ++k2) {
         hs[k2] = rem != 0;
         const uint32_t s2 = (uint32_t)__builtin_ctzll(rem | (1ull << 63));
         rem &= rem - 1ull;
@@ -1145,7 +1147,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
         x[k2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v_ml, off, 0, 0));
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
+      for (int k2 = 0; k2 < kMlPer; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
     }
     m_fin = M;
     const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
@@ -1156,11 +1158,11 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
       for (int r = 0; r < 16; ++r) o[dt][r] *= a;
     const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
     for (uint64_t rem = myrare; __ballot(rem != 0);) {
-      float2 ml[2];
-      u32x4 w4[2][8];
-      bool hs[2];
+      float2 ml[kPartPer];
+      u32x4 w4[kPartPer][8];
+      bool hs[kPartPer];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
+      for (int k2 = 0; k2 < kPartPer; ++k2) {
         hs[k2] = rem != 0;
         const uint32_t ent = tok_e + (uint32_t)__builtin_ctzll(rem | (1ull << 63));
         rem &= rem - 1ull;
@@ -1174,7 +1176,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_o, ob + i * 32 * Hpg, 0, 0));
       }
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
+      for (int k2 = 0; k2 < kPartPer; ++k2) {
         const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - M) : 0.f;
         l_run += w;
 #pragma unroll

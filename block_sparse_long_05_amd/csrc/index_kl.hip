@@ -61,19 +61,20 @@ __device__ __forceinline__ void load_row_op(u32x4* op, const uint16_t* row, int 
 
 // Pass 0 (kGrad false) or pass 1 (kGrad true) over one unit. kIndexOnly: pass 0 with the
 // main heads' log-sum-exps given by the caller, so only the index scores are reduced.
-template <bool kGrad, bool kIndexOnly = false>
-__global__ __launch_bounds__(256, 1) void kl_unit_kernel(
+// Pass 0 over one unit: per entry, (max, sum of exponentials) of each main head's scores and
+// of the index scores over the block's visible keys. kIndexOnly: the main heads'
+// log-sum-exps are given by the caller, so only the index scores are reduced. Four waves
+// take the unit's 32-entry groups in turn; two workgroups share a CU (65 KiB of LDS).
+template <bool kIndexOnly>
+__global__ __launch_bounds__(256, 2) void kl_stats_unit_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ QI, const uint16_t* __restrict__ KI,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ offset,
     const int32_t* __restrict__ unit_off, const int32_t* __restrict__ unit_bucket, int64_t nb,
     int nblk, int G, int Hpg, int top_k, int64_t q_begin, int64_t seq_len, float index_scale,
-    float* __restrict__ part_stats, const float* __restrict__ lse, float* __restrict__ part_loss,
-    float* __restrict__ part_dq, float* __restrict__ part_dk) {
-  __shared__ __align__(16) uint8_t Kb[kBlock * kRowBytes];
+    float* __restrict__ part_stats) {
+  __shared__ __align__(16) uint8_t Kb[kIndexOnly ? 16 : kBlock * kRowBytes];
   __shared__ __align__(16) uint8_t KIb[kBlock * kRowBytes];
-  __shared__ __align__(16) uint8_t Wb[kGrad ? 4 * kWaveTile : 16];   // per wave: W tile
-  __shared__ __align__(16) uint8_t QIb[kGrad ? 4 * kWaveTile : 16];  // per wave: q_idx rows
   __shared__ int32_t ids[kUnit];
 
   const int tid = threadIdx.x;
@@ -96,165 +97,218 @@ __global__ __launch_bounds__(256, 1) void kl_unit_kernel(
   const float c_idx = kLog2e * index_scale;
   const int Hq = G * Hpg;
   const int ngroups = (n + 31) / 32;
-  const int nrounds = (ngroups + 3) / 4;
-  f32x16 dk[4] = {};
 
-  for (int rd = 0; rd < nrounds; ++rd) {
-    const int grp = 4 * rd + wave;
-    if (grp < ngroups) {
-      const int ent = 32 * grp + n32;
-      const bool ok = ent < n;
-      const int32_t id = ok ? ids[ent] : 0;
-      const int64_t rowg = id / top_k;                 // chunk row * G + g
-      const int64_t t = q_begin + rowg / G;
-      // last visible key offset in the block, folded with the lane's key offset 4q
-      const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
-      const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
-      const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
-      u32x4 qiop[kHeadDim / 16];
-      load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
-
-      if constexpr (!kGrad) {
-        for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
-          u32x4 qop[kHeadDim / 16];
-          if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q, ok);
-          const float sc = h < Hpg ? c_main : c_idx;
-          f32x16 sv[4];
-          float mx = -INFINITY;
-          int lq = limq;
-          asm volatile("" : "+v"(lq));
+  for (int grp = wave; grp < ngroups; grp += 4) {
+    const int ent = 32 * grp + n32;
+    const bool ok = ent < n;
+    const int32_t id = ok ? ids[ent] : 0;
+    const int64_t rowg = id / top_k;                 // chunk row * G + g
+    const int64_t t = q_begin + rowg / G;
+    // last visible key offset in the block, folded with the lane's key offset 4q
+    const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
+    const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
+    const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
+    u32x4 qiop[kHeadDim / 16];
+    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
+    for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
+      u32x4 qop[kHeadDim / 16];
+      if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q, ok);
+      const float sc = h < Hpg ? c_main : c_idx;
+      f32x16 sv[4];
+      float mx = -INFINITY;
+      int lq = limq;
+      asm volatile("" : "+v"(lq));
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            sv[kt] = h < Hpg ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
-                             : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
+      for (int kt = 0; kt < 4; ++kt) {
+        sv[kt] = h < Hpg ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
+                         : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float x = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? sv[kt][r] * sc : -INFINITY;
-              sv[kt][r] = x;
-              mx = fmaxf(mx, x);
-            }
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          float l = 0.f;
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) l += fast_exp2(sv[kt][r] - mx);
-          l += __shfl_xor(l, 32, 64);
-          if (ok && q == 0)
-            *reinterpret_cast<float2*>(part_stats + ((int64_t)id * (Hpg + 1) + h) * 2) =
-                make_float2(mx, l);
-        }
-      } else {
-        const float* lrow = lse + rowg * (Hpg + 1);
-        float w[4][16];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) w[kt][r] = 0.f;
-        // P: mean over the group's heads of each head's probabilities
-        for (int h = 0; h < Hpg; ++h) {
-          u32x4 qop[kHeadDim / 16];
-          load_row_op(qop, qrow + h * kHeadDim, q, ok);
-          const float lh = ok ? lrow[h] : 0.f;
-          // the causal compares are redone per head (two VALU ops per score) rather than
-          // kept as 64 hoisted lane masks, which the compiler would spill
-          int lq = limq;
-          asm volatile("" : "+v"(lq));
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float e = fast_exp2(fmaf(sv[r], c_main, -lh));
-              w[kt][r] += 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? e : 0.f;
-            }
-          }
-        }
-        const float inv_h = 1.f / (float)Hpg;
-        const float li = ok ? lrow[Hpg] : 0.f;
-        float lsum = 0.f;
-        int lq = limq;
-        asm volatile("" : "+v"(lq));
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const f32x16 xv = s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = w[kt][r] * inv_h;             // 0 for keys the row cannot see
-            const float z = fmaf(xv[r], c_idx, -li);      // log2 I
-            const float iv = fast_exp2(z);
-            // P ln(P / I) in log2 units; p = 0 gives 0 (the clamp only keeps the log finite)
-            lsum += p * (__builtin_amdgcn_logf(fmaxf(p, 1e-30f)) - z);
-            w[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? index_scale * (iv - p) : 0.f;
-          }
-        }
-        lsum += __shfl_xor(lsum, 32, 64);
-        if (ok && q == 0) part_loss[id] = lsum * kLn2;
-        // dq^T = K_idx^T . W^T over the block's two 64-key halves
-        f32x16 o[4] = {};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 pb[4];
-#pragma unroll
-          for (int uu = 0; uu < 4; ++uu) {
-            const float* pr = &w[2 * half + (uu >> 1)][8 * (uu & 1)];
-            pb[uu] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                           pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
-          }
-          pv_half_tr(o, pb, KIb, lane, half);
-        }
-        if (ok) {
-          float* dst = part_dq + (int64_t)id * kHeadDim + 4 * q;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * j) =
-                  f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
-        }
-        // this wave's W (32 entries x 128 keys) and q_idx rows into LDS, V swizzle
-        uint8_t* wrow = Wb + wave * kWaveTile + n32 * kRowBytes;
-        const int sw = v_swz(n32);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<u32x2*>(wrow + (((4 * kt + j) ^ sw) * 16) + 8 * q) =
-                u32x2{pack_bf16x2(w[kt][4 * j], w[kt][4 * j + 1]),
-                      pack_bf16x2(w[kt][4 * j + 2], w[kt][4 * j + 3])};
-        uint8_t* qrow_l = QIb + wave * kWaveTile + n32 * kRowBytes;
-#pragma unroll
-        for (int s = 0; s < kHeadDim / 16; ++s)
-          *reinterpret_cast<u32x4*>(qrow_l + ((2 * s + q) ^ sw) * 16) = qiop[s];
-      }
-    }
-    if constexpr (kGrad) {
-      __syncthreads();
-      // dk (keys 32 wave + C rows, d 32 dn + column) += W^T . q_idx over this round's entries
-      for (int src = 0; src < 4; ++src) {
-        if (4 * rd + src >= ngroups) break;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 a = tr_operand(Wb + src * kWaveTile, 16 * ks, wave, lane);
-#pragma unroll
-          for (int dn = 0; dn < 4; ++dn)
-            dk[dn] = mfma32(a, tr_operand(QIb + src * kWaveTile, 16 * ks, dn, lane), dk[dn]);
+        for (int r = 0; r < 16; ++r) {
+          const float x = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? sv[kt][r] * sc : -INFINITY;
+          sv[kt][r] = x;
+          mx = fmaxf(mx, x);
         }
       }
-      __syncthreads();
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float l = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) l += fast_exp2(sv[kt][r] - mx);
+      l += __shfl_xor(l, 32, 64);
+      if (ok && q == 0)
+        *reinterpret_cast<float2*>(part_stats + ((int64_t)id * (Hpg + 1) + h) * 2) =
+            make_float2(mx, l);
     }
   }
-  if constexpr (kGrad) {
-    float* dst = part_dk + (int64_t)u * kBlock * kHeadDim;
+}
+
+// Pass 1 over one unit: per entry, P (head mean, from the row's log-sum-exps) and I for the
+// block's keys, the entry's loss term, W = index_scale (I - P) and its dq_idx partial
+// (K_idx^T . W^T, the transpose read of the main branch's PV product); per unit, the block's
+// dk_idx partial W^T . q_idx. Eight waves (two per SIMD): wave w takes entries
+// 32 w .. 32 w + 31, so a unit of at most 256 entries is a single round. W is rounded to
+// bf16 once and serves both products. The block's key gradient is split over the waves
+// (wave w: keys 32 (w % 4) + 0..31, dims 64 (w / 4) + 0..63); the waves' W and q_idx tiles
+// reach it through LDS in two halves (waves 0-3, then 4-7) sharing one exchange area, in the
+// unit's entry order.
+__global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ QI, const uint16_t* __restrict__ KI,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ offset,
+    const int32_t* __restrict__ unit_off, const int32_t* __restrict__ unit_bucket, int64_t nb,
+    int nblk, int G, int Hpg, int top_k, int64_t q_begin, int64_t seq_len, float index_scale,
+    const float* __restrict__ lse, float* __restrict__ part_loss, float* __restrict__ part_dq,
+    float* __restrict__ part_dk) {
+  __shared__ __align__(16) uint8_t Kb[kBlock * kRowBytes];
+  __shared__ __align__(16) uint8_t KIb[kBlock * kRowBytes];
+  __shared__ __align__(16) uint8_t Wb[4 * kWaveTile];   // per publishing wave: W tile
+  __shared__ __align__(16) uint8_t QIb[4 * kWaveTile];  // per publishing wave: q_idx rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int u = blockIdx.x;
+  if (u >= unit_off[nb]) return;
+  const int k = __builtin_amdgcn_readfirstlane(unit_bucket[u]);
+  const int g = k / nblk;
+  const int c = k - g * nblk;
+  const int e0 = offset[k] + kUnit * (u - unit_off[k]);
+  const int n = min(kUnit, offset[k + 1] - e0);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  k_block_dma_s<512>(K, g, c, seq_len, Kb, wv, dma_lane_off<false>(lane), tid);
+  k_block_dma_s<512, true>(KI, 0, c, seq_len, KIb, wv, dma_lane_off<true>(lane), tid);
+
+  const int n32 = lane & 31, q = lane >> 5;
+  const int ent = 32 * wave + n32;
+  const bool ok = ent < n;
+  const int32_t id = ok ? sorted[e0 + ent] : 0;
+  MSA_WAIT_VMCNT(0);
+  __syncthreads();
+
+  const float c_main = kLog2e / sqrtf((float)kHeadDim);
+  const float c_idx = kLog2e * index_scale;
+  const int Hq = G * Hpg;
+  const int ngroups = (n + 31) / 32;
+  const bool active = wave < ngroups;  // wave-uniform
+  uint32_t wp[4][8];                   // W (bf16 pairs) of the lane's 64 keys
+  u32x4 qiop[kHeadDim / 16];
+  if (active) {
+    const int64_t rowg = id / top_k;  // chunk row * G + g
+    const int64_t t = q_begin + rowg / G;
+    const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
+    const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
+    const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
+    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
+    const float* lrow = lse + rowg * (Hpg + 1);
+    float w[4][16];
 #pragma unroll
-    for (int dn = 0; dn < 4; ++dn)
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w[kt][r] = 0.f;
+    // P: mean over the group's heads of each head's probabilities
+    for (int h = 0; h < Hpg; ++h) {
+      u32x4 qop[kHeadDim / 16];
+      load_row_op(qop, qrow + h * kHeadDim, q, ok);
+      const float lh = ok ? lrow[h] : 0.f;
+      // the causal compares are redone per head (two VALU ops per score) rather than
+      // kept as 64 hoisted lane masks, which the compiler would spill
+      int lq = limq;
+      asm volatile("" : "+v"(lq));
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(sv[r], c_main, -lh));
+          w[kt][r] += 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? e : 0.f;
+        }
+      }
+    }
+    const float inv_h = 1.f / (float)Hpg;
+    const float li = ok ? lrow[Hpg] : 0.f;
+    float lsum = 0.f;
+    int lq = limq;
+    asm volatile("" : "+v"(lq));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x16 xv = s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * wave + 8 * (r >> 2) + 4 * q + (r & 3);
-        dst[key * kHeadDim + 32 * dn + n32] = dk[dn][r];
+        const float p = w[kt][r] * inv_h;             // 0 for keys the row cannot see
+        const float z = fmaf(xv[r], c_idx, -li);      // log2 I
+        const float iv = fast_exp2(z);
+        // P ln(P / I) in log2 units; p = 0 gives 0 (the clamp only keeps the log finite)
+        lsum += p * (__builtin_amdgcn_logf(fmaxf(p, 1e-30f)) - z);
+        w[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? index_scale * (iv - p) : 0.f;
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wp[kt][i] = pack_bf16x2(w[kt][2 * i], w[kt][2 * i + 1]);
+    }
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (ok && q == 0) part_loss[id] = lsum * kLn2;
+    // dq^T = K_idx^T . W^T over the block's two 64-key halves
+    f32x16 o[4] = {};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4 pb[4];
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const uint32_t* pr = &wp[2 * half + (uu >> 1)][4 * (uu & 1)];
+        pb[uu] = u32x4{pr[0], pr[1], pr[2], pr[3]};
+      }
+      pv_half_tr(o, pb, KIb, lane, half);
+    }
+    if (ok) {
+      float* dst = part_dq + (int64_t)id * kHeadDim + 4 * q;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * j) =
+              f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+    }
   }
+  // dk (keys 32 (wave % 4) + C rows, dims 64 (wave / 4) + 32 dn + column) += W^T . q_idx
+  f32x16 dk[2] = {};
+  const int kq = wave & 3, dq0 = 2 * (wave >> 2);
+#pragma unroll
+  for (int hx = 0; hx < 2; ++hx) {
+    if (hx == 1) __syncthreads();  // every wave is done reading the first half's tiles
+    if ((wave >> 2) == hx && active) {
+      // this wave's W (32 entries x 128 keys) and q_idx rows into its slot, V swizzle
+      uint8_t* wrow = Wb + kq * kWaveTile + n32 * kRowBytes;
+      const int sw = v_swz(n32);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<u32x2*>(wrow + (((4 * kt + j) ^ sw) * 16) + 8 * q) =
+              u32x2{wp[kt][2 * j], wp[kt][2 * j + 1]};
+      uint8_t* qrow_l = QIb + kq * kWaveTile + n32 * kRowBytes;
+#pragma unroll
+      for (int s = 0; s < kHeadDim / 16; ++s)
+        *reinterpret_cast<u32x4*>(qrow_l + ((2 * s + q) ^ sw) * 16) = qiop[s];
+    }
+    __syncthreads();
+    for (int src = 0; src < 4; ++src) {
+      if (4 * hx + src >= ngroups) break;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 a = tr_operand(Wb + src * kWaveTile, 16 * ks, kq, lane);
+#pragma unroll
+        for (int dn = 0; dn < 2; ++dn)
+          dk[dn] = mfma32(a, tr_operand(QIb + src * kWaveTile, 16 * ks, dq0 + dn, lane), dk[dn]);
+      }
+    }
+  }
+  float* dst = part_dk + (int64_t)u * kBlock * kHeadDim;
+#pragma unroll
+  for (int dn = 0; dn < 2; ++dn)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kq + 8 * (r >> 2) + 4 * q + (r & 3);
+      dst[key * kHeadDim + 32 * (dq0 + dn) + n32] = dk[dn][r];
+    }
 }
 
 // Row log-sum-exps (log2 units) of the main heads and the index scores from the partials of
@@ -400,20 +454,20 @@ hipError_t launch_index_kl_prefill(const void* q, const void* k, const void* q_i
   const uint16_t* QI = static_cast<const uint16_t*>(q_idx);
   const uint16_t* KI = static_cast<const uint16_t*>(k_idx);
   if (main_lse != nullptr)
-    hipLaunchKernelGGL((kl_unit_kernel<false, true>), dim3((unsigned)U), dim3(256), 0, st, Q, K,
+    hipLaunchKernelGGL((kl_stats_unit_kernel<true>), dim3((unsigned)U), dim3(256), 0, st, Q, K,
                        QI, KI, sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k,
-                       q_begin, seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
+                       q_begin, seq_len, index_scale, part_stats);
   else
-    hipLaunchKernelGGL((kl_unit_kernel<false>), dim3((unsigned)U), dim3(256), 0, st, Q, K, QI, KI,
-                       sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k, q_begin,
-                       seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
+    hipLaunchKernelGGL((kl_stats_unit_kernel<false>), dim3((unsigned)U), dim3(256), 0, st, Q, K,
+                       QI, KI, sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k,
+                       q_begin, seq_len, index_scale, part_stats);
   const int64_t rows_g = q_count * G;
   const unsigned grid_s = (unsigned)std::min<int64_t>((rows_g * (Hpg + 1) + 255) / 256, 65536);
   hipLaunchKernelGGL(kl_stats_fold_kernel, dim3(grid_s), dim3(256), 0, st, block_idx, part_stats,
                      main_lse, lse, rows_g, G, Hpg, top_k, q_begin);
-  hipLaunchKernelGGL((kl_unit_kernel<true>), dim3((unsigned)U), dim3(256), 0, st, Q, K, QI, KI,
+  hipLaunchKernelGGL(kl_grad_unit_kernel, dim3((unsigned)U), dim3(512), 0, st, Q, K, QI, KI,
                      sorted, offset, unit_off, unit_bucket, nb, nblk, G, Hpg, top_k, q_begin,
-                     seq_len, index_scale, part_stats, lse, part_loss, part_dq, part_dk);
+                     seq_len, index_scale, lse, part_loss, part_dq, part_dk);
   const unsigned grid_g = (unsigned)std::min<int64_t>((rows_g * 32 + 255) / 256, 65536);
   hipLaunchKernelGGL(kl_grad_fold_kernel, dim3(grid_g), dim3(256), 0, st, block_idx, part_loss,
                      part_dq, loss, dq_idx, rows_g, G, top_k, q_begin);
