@@ -171,7 +171,8 @@ def measured_traffic(kernel_fragment):
         t = json.load(open(path))
         for name, v in t["kernels"].items():
             if kernel_fragment in name:
-                if v.get("source_hash") != source_hash(name):
+                h = source_hash(name)
+                if h is None or v.get("source_hash") != h:
                     return None
                 if v.get("read_bytes") is None or v.get("write_bytes") is None:
                     return None

@@ -30,21 +30,30 @@ CSRC = os.path.join(PKG, "csrc")
 KERNEL_SOURCES = {
     "index_scores_prefill": "index_scores.hip",
     "index_scores_decode": "index_scores.hip",
+    "index_topk": "index_scores.hip",
     "block_topk": "block_topk.hip",
     "kv_": "attn_tile.hip",
     "qtile_attn": "attn_tile.hip",
     "dense_attn": "attn_tile.hip",
     "gather_attn": "attn_gather.hip",
     "decode_combine": "attn_gather.hip",
+    "kl_": "index_kl.hip",
 }
+# device headers every kernel source includes: a change there can change any kernel
+SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h")
 
 
 def source_hash(kernel_name: str):
+    """Hash of the kernel's source file and the shared device headers; None for a kernel
+    this table does not know (its stored traffic is then never taken as current)."""
     for frag, src in KERNEL_SOURCES.items():
         if frag in kernel_name:
-            path = os.path.join(CSRC, src)
-            if os.path.exists(path):
-                return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+            h = hashlib.sha256()
+            for f in (src,) + SHARED_HEADERS:
+                path = os.path.join(CSRC, f)
+                if os.path.exists(path):
+                    h.update(open(path, "rb").read())
+            return h.hexdigest()[:16]
     return None
 
 
