@@ -159,16 +159,19 @@ class KernelTimer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
-def measured_traffic(kernel_fragment):
+def measured_traffic(kernel_fragment, kind, launch):
     """HBM bytes per launch of a kernel from profiles/traffic.json (two rocprofv3 --pmc
-    runs, scaled by a plain copy), or None when absent or when the kernel's source has
-    changed since the counters were taken."""
+    runs, scaled by a plain copy), or None when absent, when the kernel's source has
+    changed since the counters were taken, or when they were taken on another workload or
+    launch configuration (`launch`, this run's description of the `kind` leg)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         from block_sparse_long_05_amd.profiling import source_hash
         t = json.load(open(path))
+        if t.get("launches", {}).get(kind) != launch:
+            return None
         for name, v in t["kernels"].items():
             if kernel_fragment in name:
                 h = source_hash(name)
@@ -288,9 +291,12 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     n_idx_launch = len(ichunks) if fused else len(chunks)
     idx_tflops = idx_flops / n_idx_launch / (idx_ms_launch * 1e-3) / 1e12
     total_tflops = (idx_flops + att_flops) / (ms * 1e-3) / 1e12
+    # the workload and launch configuration (what the stored HBM counters must match)
+    launch = (f"{name} chunk={chunk} index_rows={ichunk} algo={args.algo} "
+              f"index={'fused' if fused else 'separate'}")
     res = dict(
-        workload=name, T=T, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
-        chunk=chunk, index_launch_rows=ichunk, algo=args.algo,
+        workload=name, launch=launch, T=T, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k,
+        dtype=cfg["dtype"], chunk=chunk, index_launch_rows=ichunk, algo=args.algo,
         index_branch="fused" if fused else "separate",
         ms_per_step=ms, wall_s=wall, tok_per_s=T / (ms * 1e-3),
         kernel_ms_per_step=per_kernel,
@@ -300,7 +306,7 @@ def run_prefill(name, cfg, args, torch, msa, synth):
                       kernel="index_topk_prefill" if fused else "index_scores_prefill",
                       achieved=idx_tflops, peak=peak, unit="TFLOP/s", frac=idx_tflops / peak,
                       traffic=measured_traffic("index_topk_prefill" if fused
-                                               else "index_scores_prefill"),
+                                               else "index_scores_prefill", "prefill", launch),
                       work_per_launch=idx_flops / n_idx_launch, launch_ms=idx_ms_launch),
     )
     log(f"[{name}] {ms:.3f} ms/step  {res['tok_per_s']:.4g} tok/s  kernels {per_kernel}  "
@@ -501,15 +507,16 @@ def run_decode(name, cfg, args, torch, msa, synth):
     scan_ms = timers["index_scan"].mean_ms()
     scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = dict(
-        workload=name, B=B, L=L, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k, dtype=cfg["dtype"],
-        us_per_step=ms_plain * 1e3, us_per_token=ms_plain * 1e3 / B,
+        workload=name, launch=name, B=B, L=L, G=G, Hpg=Hpg, d_idx=d_idx, top_k=top_k,
+        dtype=cfg["dtype"], us_per_step=ms_plain * 1e3, us_per_token=ms_plain * 1e3 / B,
         us_per_step_with_kernel_events=ms * 1e3, wall_s=wall,
         kernel_us={k: v.mean_ms() * 1e3 for k, v in timers.items()},
         bytes_per_step=tot_bytes, path_gbs=tot_bytes / (ms_plain * 1e-3) / 1e9,
         path_frac_of_hbm=tot_bytes / (ms_plain * 1e-3) / 1e9 / PEAK_HBM_GBS,
         roofline=dict(bound="hbm", kernel="index_scores_decode", achieved=scan_gbs,
                       peak=PEAK_HBM_GBS, unit="GB/s", frac=scan_gbs / PEAK_HBM_GBS,
-                      traffic=measured_traffic("index_scores_decode"), work_per_launch=scan_bytes, launch_ms=scan_ms),
+                      traffic=measured_traffic("index_scores_decode", "decode", name),
+                      work_per_launch=scan_bytes, launch_ms=scan_ms),
     )
     if args.paged:
         # the same step on a paged copy of the caches (pages at seeded random ids)

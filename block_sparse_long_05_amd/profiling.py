@@ -103,7 +103,16 @@ def _copy_value(means: dict, counter: str) -> float:
     return max(vals)  # the calibration copy is by far the largest dispatch
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_mib: float, cmd: str = "") -> dict:
+def bench_launches(log: str) -> dict:
+    """{'prefill': ..., 'decode': ...}: the workload and launch configuration of each leg,
+    from the JSON line bench.py printed in the profiled run."""
+    line = [x for x in open(log).read().splitlines() if x.startswith("{")][-1]
+    d = json.loads(line)
+    return {k: d[k]["launch"] for k in ("prefill", "decode") if d.get(k)}
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_mib: float, cmd: str = "",
+            bench_log: str = "") -> dict:
     fm, wm = counter_means(fetch_dir), counter_means(write_dir)
     copy_bytes = copy_mib * (1 << 20)
     f_copy = _copy_value(fm, "FETCH_SIZE") * 1024.0
@@ -120,7 +129,7 @@ def traffic(fetch_dir: str, write_dir: str, copy_mib: float, cmd: str = "") -> d
             write_bytes=None if wr is None else wr * 1024.0 * ws,
             source_hash=source_hash(name))
     return dict(copy_mib=copy_mib, fetch_scale=fs, write_scale=ws, command=cmd,
-                kernels=kernels)
+                launches=bench_launches(bench_log) if bench_log else {}, kernels=kernels)
 
 
 def traffic_text(t: dict, workloads: str = "") -> str:
@@ -151,6 +160,8 @@ def main():
     b.add_argument("--copy-mib", type=float, required=True)
     b.add_argument("--out", required=True)
     b.add_argument("--cmd", default="")
+    b.add_argument("--bench-log", default="",
+                   help="output of the profiled bench.py run (its workloads and launches)")
     c = sub.add_parser("traffic-text")
     c.add_argument("json")
     c.add_argument("--workloads", default="")
@@ -160,7 +171,7 @@ def main():
     elif args.what == "traffic-text":
         print(traffic_text(json.load(open(args.json)), args.workloads), end="")
     else:
-        t = traffic(args.fetch, args.write, args.copy_mib, args.cmd)
+        t = traffic(args.fetch, args.write, args.copy_mib, args.cmd, args.bench_log)
         with open(args.out, "w") as f:
             json.dump(t, f, indent=1)
         for k, v in t["kernels"].items():
