@@ -657,64 +657,53 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
       const int32_t cur_id = id;
       const bool cur_ok = ok;
-      float m_run = -INFINITY, l_run = 0.f;
       f32x16 o[4] = {};
+      // all four S^T tiles of the block and their maximum first: a row sees one block here,
+      // so the maximum is exact and the accumulator is never rescaled
+      float p[4][16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+        // the compare and select only where a row of the wave ends inside the block
+        if (masked) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            p[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[kt][r] = sv[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kt][r]);
+      }
+      if (rt + 4 < nrt) {  // S^T is done with this row tile's queries
+        ok = row_of(rt + 4, id, t);
+        T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_run = mx * qk_scale;  // key 128c <= t: -inf only for a lane without entry
+      const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+      float l_run = 0.f;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        float p[2][16];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int kt = 2 * half + kk2;
-          const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
-          // the compare and select only where a row of the wave ends inside the block
-          if (masked) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              p[kk2][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[kk2][r] = sv[r];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kk2][r]);
-        }
-        if (half == 1 && rt + 4 < nrt) {  // S^T is done with this row tile's queries
-          ok = row_of(rt + 4, id, t);
-          T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mxs = mx * qk_scale;
-        const bool raise = mxs > m_run + 8.f;  // the first half always sets it (key 128c <= t)
-        if (__ballot(raise)) {
-          const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
-          m_run = raise ? mxs : m_run;
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        }
-        float lsum = 0.f;
-#pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float ev = fast_exp2(fmaf(p[kk2][r], qk_scale, -m_run));
-            p[kk2][r] = ev;
-            lsum += ev;
-          }
-        lsum += __shfl_xor(lsum, 32, 64);
-        l_run += lsum;
         u32x4 pb[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float* pr = &p[u >> 1][8 * (u & 1)];
-          pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          float* pr = p[2 * half + kk2];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pr[r] = fast_exp2(fmaf(pr[r], qk_scale, mneg));
+            l_run += pr[r];
+          }
+          pb[2 * kk2] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+          pb[2 * kk2 + 1] = u32x4{pack_bf16x2(pr[8], pr[9]), pack_bf16x2(pr[10], pr[11]),
+                                  pack_bf16x2(pr[12], pr[13]), pack_bf16x2(pr[14], pr[15])};
         }
         pv_half_tr(o, pb, Vb, lane_v, half);
       }
+      l_run += __shfl_xor(l_run, 32, 64);
       if (cur_ok) {
         const float inv = 1.f / l_run;
         const int64_t prow = (int64_t)cur_id * Hpg + h;
@@ -1058,59 +1047,59 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const bool masked = __ballot(ok && lime < kBlock - 1) != 0;
     int limq = lime - 4 * qv;  // the lane's key offset 4q folded into the limit
     asm volatile("" : "+v"(limq));
-    // the block's 128 keys in two halves of 64, one online-softmax step each
+    // the block's 128 keys: all four S^T tiles and their maximum first (one test of the lazy
+    // maximum per block), then per 64-key half the exponentials, which the compiler can
+    // interleave with the other half's PV products
+    float p[4][16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const f32x16 sv = s_tile_swz(Kc, 32 * kt + n32v, qop, qv);
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          p[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[kt][r] = sv[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kt][r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mxs = mx * qk_scale;
+    const bool raise = mxs > m_run + 8.f;  // false while the row has no score (-inf)
+    if (__ballot(raise)) {
+      const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
+      m_run = raise ? mxs : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;  // masked scores give exp2(-inf) = 0
+    float lsum = 0.f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      float p[2][16];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        const int kt = 2 * half + kk2;
-        const f32x16 sv = s_tile_swz(Kc, 32 * kt + n32v, qop, qv);
-        if (masked) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            p[kk2][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= limq ? sv[r] : -INFINITY;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[kk2][r] = sv[r];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kk2][r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mxs = mx * qk_scale;
-      const bool raise = mxs > m_run + 8.f;  // false while the row has no score (-inf)
-      if (__ballot(raise)) {
-        const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
-        m_run = raise ? mxs : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      const float mneg = m_run == -INFINITY ? 0.f : -m_run;  // masked scores give exp2(-inf) = 0
-      float lsum = 0.f;
-#pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float ev = fast_exp2(fmaf(p[kk2][r], qk_scale, mneg));
-          p[kk2][r] = ev;
-          lsum += ev;
-        }
-      lsum += __shfl_xor(lsum, 32, 64);
-      l_run += lsum;
       u32x4 pb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* pr = &p[u >> 1][8 * (u & 1)];
-        pb[u] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        float* pr = p[2 * half + kk2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = fast_exp2(fmaf(pr[r], qk_scale, mneg));
+          lsum += pr[r];
+        }
+        pb[2 * kk2] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+        pb[2 * kk2 + 1] = u32x4{pack_bf16x2(pr[8], pr[9]), pack_bf16x2(pr[10], pr[11]),
+                                pack_bf16x2(pr[12], pr[13]), pack_bf16x2(pr[14], pr[15])};
       }
       pv_half_tr(o, pb, Vc, lane_v, half);
     }
+    lsum += __shfl_xor(lsum, 32, 64);
+    l_run += lsum;
   };
   for (int j = 0; j < ns; j += 2) {
     shared_block(j, Kb0, Vb0, Kb1, Vb1);
