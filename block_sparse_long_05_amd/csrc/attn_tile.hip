@@ -637,26 +637,34 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       t = q_begin + (id / top_k) / G;
       return ok;
     };
-    T::qop_t qop[T::kQSteps];
-    int32_t id = 0;
-    int64_t t = 0;
-    bool ok = false;
+    // Row tiles alternate between two query-operand buffers: the queries of row tile
+    // rt + 4 are requested as row tile rt starts, a whole row tile ahead of their use. The
+    // loads are unconditional (a lane without entry reads the chunk's first row, whose
+    // results it never stores): a load behind a lane mask would make the compiler wait for
+    // every access in flight, the previous row tile's partial stores included.
+    T::qop_t qa[T::kQSteps], qb[T::kQSteps];
+    int32_t ida = 0, idb = 0;
+    int64_t ta = 0, tb = 0;
+    bool oka = false, okb = false;
     if (wave < nrt) {
-      ok = row_of(wave, id, t);
-      T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
+      oka = row_of(wave, ida, ta);
+      T::load_q(qa, Q + (ta * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, true);
     }
     MSA_WAIT_VMCNT(0);  // this wave's K and V loads have landed
     __syncthreads();
-    for (int rt = wave; rt < nrt; rt += 4) {
+    auto row_tile = [&](int rt, const T::qop_t* qc, int32_t cur_id, int64_t tc, bool cur_ok,
+                        T::qop_t* qn, int32_t& idn, int64_t& tn, bool& okn) {
+      if (rt + 4 < nrt) {
+        okn = row_of(rt + 4, idn, tn);
+        T::load_q(qn, Q + (tn * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, true);
+      }
       int lane_v = lane;
       asm volatile("" : "+v"(lane_v));
       const int n32v = lane_v & 31, qv = lane_v >> 5;
-      const int lim = min(max((int)t - c * kBlock, -1), kBlock);
+      const int lim = min(max((int)tc - c * kBlock, -1), kBlock);
       int limq = lim - 4 * q;  // the lane's key offset 4q folded into the limit
       asm volatile("" : "+v"(limq));
-      const bool masked = __ballot(ok && lim < kBlock - 1) != 0;
-      const int32_t cur_id = id;
-      const bool cur_ok = ok;
+      const bool masked = __ballot(cur_ok && lim < kBlock - 1) != 0;
       f32x16 o[4] = {};
       // all four S^T tiles of the block and their maximum first: a row sees one block here,
       // so the maximum is exact and the accumulator is never rescaled
@@ -664,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qop, qv);
+        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qc, qv);
         // the compare and select only where a row of the wave ends inside the block
         if (masked) {
 #pragma unroll
@@ -676,10 +684,6 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, p[kt][r]);
-      }
-      if (rt + 4 < nrt) {  // S^T is done with this row tile's queries
-        ok = row_of(rt + 4, id, t);
-        T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_run = mx * qk_scale;  // key 128c <= t: -inf only for a lane without entry
@@ -722,6 +726,10 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
           }
         if (q == 0) *reinterpret_cast<float2*>(part_ml + prow * 2) = make_float2(m_run, l_run);
       }
+    };
+    for (int rt = wave; rt < nrt; rt += 8) {
+      row_tile(rt, qa, ida, ta, oka, qb, idb, tb, okb);
+      if (rt + 4 < nrt) row_tile(rt + 4, qb, idb, tb, okb, qa, ida, ta, oka);
     }
   }
 }
