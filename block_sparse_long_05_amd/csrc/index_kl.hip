@@ -53,10 +53,13 @@ __global__ void kl_unit_fill_kernel(const int32_t* __restrict__ unit_off, int64_
     for (int32_t u = unit_off[k]; u < unit_off[k + 1]; ++u) unit_bucket[u] = (int32_t)k;
 }
 
-__device__ __forceinline__ void load_row_op(u32x4* op, const uint16_t* row, int q, bool ok) {
+// One MFMA operand row of 128 bf16 values. The loads are unconditional: a lane without an
+// entry addresses the chunk's first row and has every key masked (its causal limit is -1024),
+// and a load behind a lane mask would make the compiler wait for every access in flight.
+__device__ __forceinline__ void load_row_op(u32x4* op, const uint16_t* row, int q) {
 #pragma unroll
   for (int s = 0; s < kHeadDim / 16; ++s)
-    op[s] = ok ? *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+    op[s] = *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * q);
 }
 
 // Pass 0 (kGrad false) or pass 1 (kGrad true) over one unit. kIndexOnly: pass 0 with the
@@ -109,10 +112,10 @@ __global__ __launch_bounds__(256, 2) void kl_stats_unit_kernel(
     const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
     const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
     u32x4 qiop[kHeadDim / 16];
-    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
+    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q);
     for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
       u32x4 qop[kHeadDim / 16];
-      if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q, ok);
+      if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q);
       const float sc = h < Hpg ? c_main : c_idx;
       f32x16 sv[4];
       float mx = -INFINITY;
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
     const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
     const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
     const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
-    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q, ok);
+    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q);
     const float* lrow = lse + rowg * (Hpg + 1);
     float w[4][16];
 #pragma unroll
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
     // P: mean over the group's heads of each head's probabilities
     for (int h = 0; h < Hpg; ++h) {
       u32x4 qop[kHeadDim / 16];
-      load_row_op(qop, qrow + h * kHeadDim, q, ok);
+      load_row_op(qop, qrow + h * kHeadDim, q);
       const float lh = ok ? lrow[h] : 0.f;
       // the causal compares are redone per head (two VALU ops per score) rather than
       // kept as 64 hoisted lane masks, which the compiler would spill
