@@ -212,7 +212,7 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
     for (int h = 0; h < Hpg; ++h) {
       u32x4 qop[kHeadDim / 16];
       load_row_op(qop, qrow + h * kHeadDim, q);
-      const float lh = ok ? lrow[h] : 0.f;
+      const float lh = lrow[h];  // a lane without entry reads row 0 (all its keys masked)
       // the causal compares are redone per head (two VALU ops per score) rather than
       // kept as 64 hoisted lane masks, which the compiler would spill
       int lq = limq;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
       }
     }
     const float inv_h = 1.f / (float)Hpg;
-    const float li = ok ? lrow[Hpg] : 0.f;
+    const float li = lrow[Hpg];
     float lsum = 0.f;
     int lq = limq;
     asm volatile("" : "+v"(lq));
