@@ -56,6 +56,7 @@ PREFILL_CASES = [
     (2300, 4, 8, 128, 16, "bf16", 4),   # 18 blocks > top_k = 16
     (700, 1, 16, 128, 2, "bf16", 0),    # one group, 16 heads per group
     (640, 3, 1, 64, 3, "bf16", 0),      # one head per group, G = 3
+    (1200, 2, 3, 128, 8, "bf16", 2),    # 3 heads: rows 30, 31 of every row tile unused
 ]
 
 
@@ -72,14 +73,19 @@ def test_prefill_parity(T, G, Hpg, d_idx, top_k, dtype, planted, algo):
 
 
 @pytest.mark.parametrize("algo", ["query_centric", "auto"])
-def test_prefill_chunked_rows(algo):
+@pytest.mark.parametrize("T,G,Hpg,top_k,q0,qn", [
+    (1500, 4, 8, 4, 700, 600),   # query tiles of 32 tokens that straddle block boundaries
+    (1300, 2, 3, 6, 333, 700),   # 3 heads (30-token tiles), an odd chunk start
+])
+def test_prefill_chunked_rows(algo, T, G, Hpg, top_k, q0, qn):
     """q_begin/q_count: a chunk in the middle of the sequence gives the same rows."""
-    T, G, Hpg, top_k = 1500, 4, 8, 4
-    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=77, planted_per_group=2)
-    q0, qn = 700, 600
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=77 + Hpg,
+                             planted_per_group=2)
+    print(f"prefill chunk T={T} G={G} Hpg={Hpg} k={top_k} rows [{q0}, {q0 + qn}) {algo}",
+          flush=True)
     out, idx, bs = _run_prefill(x, top_k, q_begin=q0, q_count=qn, algo=algo)
     rows = np.arange(q0, q0 + qn)
-    res = _oracle_prefill("chunk", x, top_k, rows=rows)
+    res = _oracle_prefill(("chunk", T, G, Hpg, top_k, q0, qn), x, top_k, rows=rows)
     lse = _LAST_LSE["lse"]
     parity.check_prefill(x, rows, out, idx, bs, res, top_k, q_begin=q0, label="chunk",
                          lse_gpu=lse)
