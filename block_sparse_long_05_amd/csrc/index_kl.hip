@@ -364,12 +364,17 @@ __global__ void kl_grad_fold_kernel(const int32_t* __restrict__ block_idx,
     const int64_t b = (q_begin + rg / G) / kBlock;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float ls = 0.f;
+    // every slot's partial is loaded (four slots in flight) and the invisible ones, never
+    // written, are dropped by a select rather than skipped by a branch
+#pragma unroll 4
     for (int s = 0; s < top_k; ++s) {
       const int cb = block_idx[rg * top_k + s];
-      if (cb < 0 || cb > b) continue;
+      const bool vis = cb >= 0 && cb <= b;
       const int64_t e = rg * top_k + s;
-      acc += *reinterpret_cast<const f32x4*>(part_dq + e * kHeadDim + 4 * j);
-      if (j == 0) ls += part_loss[e];
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part_dq + e * kHeadDim + 4 * j);
+      const float xl = part_loss[e];
+      acc = vis ? acc + x : acc;
+      ls = vis ? ls + xl : ls;
     }
     *reinterpret_cast<f32x4*>(dq + rg * kHeadDim + 4 * j) = acc;
     if (j == 0) loss[rg] = ls;
@@ -392,10 +397,21 @@ __global__ void kl_dk_fold_kernel(const int32_t* __restrict__ unit_off,
     bool any = false;
     for (int g = 0; g < G; ++g) {
       const int64_t kb = (int64_t)g * nblk + c;
-      for (int32_t uu = unit_off[kb]; uu < unit_off[kb + 1]; ++uu) {
-        acc += *reinterpret_cast<const f32x4*>(part_dk + ((int64_t)uu * kBlock + j) * kHeadDim + 4 * v);
-        any = true;
+      const int32_t u0 = unit_off[kb], u1 = unit_off[kb + 1];
+      any = any || u1 > u0;
+      // the bucket's units in groups of four (four partial rows in flight), summed in order
+      int32_t uu = u0;
+      for (; uu + 4 <= u1; uu += 4) {
+        f32x4 x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[i] = *reinterpret_cast<const f32x4*>(
+              part_dk + ((int64_t)(uu + i) * kBlock + j) * kHeadDim + 4 * v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc += x[i];
       }
+      for (; uu < u1; ++uu)
+        acc += *reinterpret_cast<const f32x4*>(part_dk + ((int64_t)uu * kBlock + j) * kHeadDim + 4 * v);
     }
     if (any) {
       f32x4* d = reinterpret_cast<f32x4*>(dk + key * kHeadDim + 4 * v);
