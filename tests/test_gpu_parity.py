@@ -57,6 +57,7 @@ PREFILL_CASES = [
     (700, 1, 16, 128, 2, "bf16", 0),    # one group, 16 heads per group
     (640, 3, 1, 64, 3, "bf16", 0),      # one head per group, G = 3
     (1200, 2, 3, 128, 8, "bf16", 2),    # 3 heads: rows 30, 31 of every row tile unused
+    (3500, 2, 2, 128, 24, "bf16", 3),   # top_k 24 > 16: the two-step index branch, wide lists
 ]
 
 
@@ -193,6 +194,7 @@ DECODE_CASES = [
     (2, 4000, [4000, 2900], 8, 8, 128, 16, "bf16", 16),
     (2, 2000, [2000, 1280], 2, 3, 64, 4, "f32", 0),
     (4, 1000, [1000, 999, 129, 128], 4, 16, 128, 3, "bf16", 2),
+    (2, 5000, [5000, 3333], 4, 8, 128, 40, "bf16", 4),  # top_k 40; 27 blocks < k: all kept
 ]
 
 
