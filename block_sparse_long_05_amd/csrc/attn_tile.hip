@@ -561,8 +561,8 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
 // ---- reverse-index tile attention, bf16 ----------------------------------------------------
 // K and V of each run's block are staged row-major by direct global->LDS loads into one
 // 64 KB buffer, so two workgroups share a CU and one's staging and query gathers overlap
-// the other's MFMA work. Each row tile covers the block in two 64-key halves with the
-// lazily raised maximum of the query-tile kernel. An entry's partial (Hpg heads x 128
+// the other's MFMA work. A row tile sees one block: its four S tiles give the exact block
+// maximum, then the exponentials and PV run per 64-key half. An entry's partial (Hpg heads x 128
 // values, bf16) is one lane-interleaved block: the 16-byte chunk i (values
 // 32 (i / 2) + 8 (i % 2) .. of the lane's fragment) of head h, lane group q sits at
 // element i * 16 Hpg + 8 (h + Hpg q), so each store instruction writes whole cache lines.
