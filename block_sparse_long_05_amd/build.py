@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmsa.so")
 
 SOURCES = ["msa_api.hip", "index_scores.hip", "block_topk.hip", "attn_gather.hip",
-           "attn_tile.hip", "index_kl.hip"]
+           "attn_tile.hip", "index_kl.hip", "decode_attn.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -50,11 +50,16 @@ int64_t nblk_of(const msa_problem* p) {
   return ceil_div(p->mode == MSA_MODE_PREFILL ? p->seq_len : p->max_len, MSA_BLOCK_SIZE);
 }
 
-// Decode split-K plan: sparse uses one half (64 keys) of one kept block per split;
-// dense spreads the cache blocks so that the launch has a few thousand waves.
+// Decode split-K plan: sparse bf16 uses one kept block per split (the block kernel of
+// decode_attn.hip), sparse fp32 one half (64 keys) of one kept block per split; dense
+// spreads the cache blocks so that the launch has a few thousand waves.
+bool decode_block_kernel(const msa_problem* p, bool dense) {
+  return !dense && p->dtype == MSA_DTYPE_BF16;
+}
+
 void decode_split(const msa_problem* p, bool dense, int* nsplit, int* bps) {
   if (!dense) {
-    *nsplit = 2 * p->top_k;
+    *nsplit = decode_block_kernel(p, dense) ? p->top_k : 2 * p->top_k;
     *bps = 1;
     return;
   }
@@ -99,9 +104,18 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             align_up(units * MSA_HEAD_DIM * sizeof(float)));
+  const int bf16 = p->dtype == MSA_DTYPE_BF16;
+  if (decode_block_kernel(p, dense)) {
+    hipError_t e = launch_decode_attn_bf16(q, k, v, block_idx, p->seq_lens, p->batch,
+                                           p->max_len, p->num_groups, p->heads_per_group,
+                                           p->top_k, pm, part_o, part_ml, st);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(launch_decode_combine(bf16, part_o, part_ml, out, p->batch,
+                                            p->num_groups, p->heads_per_group, nsplit, st));
+  }
   GatherParams gp = {};
   gp.mode = dense ? kDecodeDense : kDecodeSparse;
-  gp.bf16 = p->dtype == MSA_DTYPE_BF16;
+  gp.bf16 = bf16;
   gp.q = q;
   gp.k = k;
   gp.v = v;

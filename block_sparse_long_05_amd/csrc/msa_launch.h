@@ -74,6 +74,13 @@ struct GatherParams {
 
 hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);
 
+// Sparse decode attention, bf16 (decode_attn.hip): one partial per (sequence, group, kept
+// block) into part_o [B * G * top_k][Hpg][128] / part_ml [..][Hpg][2].
+hipError_t launch_decode_attn_bf16(const void* q, const void* k, const void* v,
+                                   const int32_t* block_idx, const int32_t* seq_lens, int B,
+                                   int64_t max_len, int G, int Hpg, int top_k, PageMap pm,
+                                   float* part_o, float* part_ml, hipStream_t st);
+
 // Fixed-order log-sum-exp merge of decode partials into out [B, Hq, 128].
 hipError_t launch_decode_combine(int bf16, const float* part_o, const float* part_ml, void* out,
                                  int B, int G, int Hpg, int nsplit, hipStream_t stream);

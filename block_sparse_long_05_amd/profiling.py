@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "gather_attn": "attn_gather.hip",
     "decode_combine": "attn_gather.hip",
     "kl_": "index_kl.hip",
+    "decode_attn": "decode_attn.hip",
 }
 # device headers every kernel source includes: a change there can change any kernel
 SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h")

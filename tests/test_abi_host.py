@@ -119,10 +119,16 @@ def test_decode_validation_and_workspace():
     c = _decode()
     assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
                                   ctypes.byref(n)) == msa.MSA_OK
-    # B * G * (2 * top_k half-block splits) * Hpg heads * (128 + 2) floats, each part
+    # bf16: B * G * (top_k block splits) * Hpg heads * (128 + 2) floats, each part
     # 256-byte aligned
-    units = 4 * 8 * 32 * 8
+    units = 4 * 8 * 16 * 8
     assert n.value == units * 128 * 4 + ((units * 2 * 4 + 255) // 256) * 256
+    # fp32: two half-block splits per kept block
+    n32 = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(_decode(dtype="f32")),
+                                  msa.ENTRY["sparse_attn_decode"], ctypes.byref(n32)) == msa.MSA_OK
+    units32 = 4 * 8 * 32 * 8
+    assert n32.value == units32 * 128 * 4 + ((units32 * 2 * 4 + 255) // 256) * 256
     # too small a workspace is refused before launching
     assert lib.msa_sparse_attn_decode(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       n.value - 1, 0) == msa.MSA_ERR_WORKSPACE_TOO_SMALL
