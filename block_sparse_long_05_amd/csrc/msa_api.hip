@@ -77,6 +77,12 @@ size_t decode_ws_bytes(const msa_problem* p, bool dense) {
   return align_up(units * MSA_HEAD_DIM * sizeof(float)) + align_up(units * 2 * sizeof(float));
 }
 
+// The KV-centric prefill and the KL loss sort the kept entries (row, group, slot) by 32-bit
+// entry id: the chunk must hold fewer than 2^31 of them.
+bool entries_fit_int32(const msa_problem* p) {
+  return (int64_t)p->q_count * p->num_groups * p->top_k < (int64_t(1) << 31);
+}
+
 size_t prefill_kv_ws_bytes(const msa_problem* p) {
   return kv_workspace_bytes(p->dtype == MSA_DTYPE_BF16, p->q_count, p->num_groups,
                             p->heads_per_group, p->top_k, (int)nblk_of(p));
@@ -167,7 +173,9 @@ msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes
       return MSA_OK;
     case MSA_ENTRY_SPARSE_ATTN_PREFILL:
       if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
-      if (p->algo != MSA_ALGO_QUERY_CENTRIC) *bytes = prefill_kv_ws_bytes(p);
+      if (p->algo == MSA_ALGO_KV_CENTRIC && !entries_fit_int32(p)) return MSA_ERR_UNSUPPORTED;
+      if (p->algo != MSA_ALGO_QUERY_CENTRIC && entries_fit_int32(p))
+        *bytes = prefill_kv_ws_bytes(p);
       return MSA_OK;
     case MSA_ENTRY_SPARSE_ATTN_DECODE:
       if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
@@ -178,6 +186,7 @@ msa_status msa_workspace_size(const msa_problem* p, int32_t entry, size_t* bytes
       return MSA_OK;
     case MSA_ENTRY_INDEX_KL:
       if (p->mode != MSA_MODE_PREFILL) return MSA_ERR_INVALID_ARGUMENT;
+      if (!entries_fit_int32(p)) return MSA_ERR_UNSUPPORTED;
       *bytes = kl_ws_bytes(p);
       return MSA_OK;
     default:
@@ -242,9 +251,11 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
     return MSA_ERR_INVALID_ARGUMENT;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return MSA_ERR_INVALID_ARGUMENT;
   if (p->q_count == 0) return MSA_OK;
-  // KV-centric when asked for, or by default when the caller's workspace can hold it.
+  // KV-centric when asked for, or by default when the caller's workspace can hold it (and
+  // the chunk's kept entries fit 32-bit ids; otherwise the query-centric path runs).
   bool kv = p->algo == MSA_ALGO_KV_CENTRIC;
-  if (p->algo != MSA_ALGO_QUERY_CENTRIC) {
+  if (kv && !entries_fit_int32(p)) return MSA_ERR_UNSUPPORTED;
+  if (p->algo != MSA_ALGO_QUERY_CENTRIC && entries_fit_int32(p)) {
     const size_t need = prefill_kv_ws_bytes(p);
     const bool fits = workspace != nullptr && workspace_bytes >= need;
     if (kv && !fits) return workspace == nullptr && workspace_bytes >= need
@@ -293,6 +304,7 @@ msa_status msa_index_kl_prefill(const msa_problem* p, const void* q, const void*
   if (main_lse != nullptr && (reinterpret_cast<uintptr_t>(main_lse) & 3u) != 0)
     return MSA_ERR_INVALID_ARGUMENT;
   if (p->q_count == 0) return MSA_OK;
+  if (!entries_fit_int32(p)) return MSA_ERR_UNSUPPORTED;  // chunk the rows
   if (workspace_bytes < kl_ws_bytes(p)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
   return hip_status(launch_index_kl_prefill(q, k, q_idx, k_idx, block_idx, main_lse, index_scale,

@@ -147,7 +147,10 @@ msa_status msa_index_topk(const msa_problem* p, const void* q_idx, const void* k
  * aligned) and receives, for the same rows, lse[t, h] = ln sum_j exp(q[t, h] . k[g, j] /
  * sqrt(D)) over the same tokens (the softmax normaliser a backward pass or the index-branch
  * KL loss needs; -inf for a row with no visible kept token). workspace may be NULL when
- * msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_PREFILL) is 0 for the chosen algo.
+ * msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_PREFILL) is 0 for the chosen algo. The
+ * KV-centric algo sorts the chunk's q_count * G * top_k kept entries by 32-bit id: with
+ * 2^31 or more of them MSA_ALGO_AUTO runs the query-centric path and MSA_ALGO_KV_CENTRIC
+ * returns MSA_ERR_UNSUPPORTED (call it on smaller row chunks).
  */
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
                                    const void* v, const int32_t* block_idx, void* out, float* lse,
@@ -204,7 +207,8 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, con
  * tensors as for msa_sparse_attn_prefill); block_idx int32 [q_count, G, top_k]; loss fp32
  * [q_count, G] and dq_idx fp32 [q_count, G, 128] are written; dk_idx fp32 [T, 128] is
  * ADDED to (the caller zeroes it once, so the chunks of one sequence accumulate).
- * Built for dtype bf16, index_dim 128 and mode prefill (else MSA_ERR_UNSUPPORTED);
+ * Built for dtype bf16, index_dim 128 and mode prefill, with fewer than 2^31 kept entries
+ * q_count * G * top_k per call (else MSA_ERR_UNSUPPORTED: call it on smaller row chunks);
  * index_scale must be finite and > 0 (else MSA_ERR_INVALID_ARGUMENT). Loss and dq_idx are
  * bit-identical from run to run; dk_idx sums each block's entries in the order the
  * reverse index places them, which may vary from run to run at the level of fp32 rounding.

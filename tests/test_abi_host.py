@@ -225,3 +225,32 @@ def test_index_kl_validation():
     m = ctypes.c_size_t(0)
     assert lib.msa_workspace_size(ctypes.byref(_decode()), msa.ENTRY["index_kl"],
                                   ctypes.byref(m)) == msa.MSA_ERR_INVALID_ARGUMENT
+
+
+def test_entry_count_limit_of_the_reverse_index():
+    """The KV-centric prefill and the KL loss sort a chunk's q_count * G * top_k kept entries
+    by 32-bit id: from 2^31 entries on, the KV-centric algo and the KL entry refuse the call
+    (before any launch) and the default algo needs no workspace (it runs query-centric)."""
+    lib = msa.load_library()
+    big = dict(seq_len=1 << 30, q_begin=0, q_count=1 << 30, num_groups=64, top_k=64)
+    n = ctypes.c_size_t(7)
+    assert lib.msa_workspace_size(ctypes.byref(_prefill(**big).c()), msa.ENTRY["index_kl"],
+                                  ctypes.byref(n)) == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_workspace_size(ctypes.byref(_prefill(algo="kv_centric", **big).c()),
+                                  msa.ENTRY["sparse_attn_prefill"],
+                                  ctypes.byref(n)) == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_workspace_size(ctypes.byref(_prefill(**big).c()),
+                                  msa.ENTRY["sparse_attn_prefill"], ctypes.byref(n)) == msa.MSA_OK
+    assert n.value == 0
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(_prefill(algo="kv_centric", **big).c()),
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, 0) \
+        == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_index_kl_prefill(ctypes.byref(_prefill(**big).c()), FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, 0, ctypes.c_float(0.1), FAKE, FAKE, FAKE, FAKE,
+                                    1 << 40, 0) == msa.MSA_ERR_UNSUPPORTED
+    # just under the limit the KV-centric workspace is sized as usual
+    under = dict(seq_len=1 << 22, q_begin=0, q_count=(1 << 31) // (64 * 64) - 1, num_groups=64,
+                 top_k=64)
+    assert lib.msa_workspace_size(ctypes.byref(_prefill(algo="kv_centric", **under).c()),
+                                  msa.ENTRY["sparse_attn_prefill"], ctypes.byref(n)) == msa.MSA_OK
+    assert n.value > 0
