@@ -315,6 +315,22 @@ def run_prefill(name, cfg, args, torch, msa, synth):
     if args.kl and cfg["dtype"] == "bf16" and d_idx == 128:
         res["kl"] = run_kl(name, cfg, args, torch, msa, x, idx_full, chunks, T, G, Hpg, d_idx,
                            top_k, peak)
+    if cfg["dtype"] == "bf16" and args.gemm_calibration:
+        # The card's practical bf16 MFMA rate on the same kind of data, outside the timed
+        # region: the vendor GEMM (torch.matmul -> hipBLASLt) on N(0,1) operands. The spec
+        # peak is not sustained on random data (the clock drops under dense MFMA load).
+        n = 16384
+        ga = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        gb = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+        gemm_ms = time_reps(torch, lambda: torch.matmul(ga, gb), 5)
+        del ga, gb
+        gemm_tflops = 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12
+        res["measured_bf16_gemm_tflops"] = gemm_tflops
+        res["path_frac_of_measured_gemm"] = total_tflops / gemm_tflops
+        res["roofline"]["frac_of_measured_gemm"] = idx_tflops / gemm_tflops
+        log(f"[{name}] vendor bf16 GEMM {n}^3 on N(0,1) data: {gemm_tflops:.0f} TFLOP/s; path "
+            f"{res['path_frac_of_measured_gemm'] * 100:.1f}% of it, index kernel "
+            f"{res['roofline']['frac_of_measured_gemm'] * 100:.1f}%")
     if args.dense_reps > 0:
         # dense causal GQA attention over the same rows (the speedup context): same chunks
         dout = torch.empty_like(q)  # its own output: `out` is checked against the oracle below
@@ -624,6 +640,9 @@ def main():
                     help="timed runs of the dense GQA entry point on the same workload "
                          "(speedup context; 0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--gemm-calibration", type=int, default=1,
+                    help="also time the vendor bf16 GEMM (16384^3, N(0,1) operands) and report "
+                         "the prefill path against it (1/0)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
