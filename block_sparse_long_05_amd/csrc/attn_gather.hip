@@ -291,8 +291,8 @@ __global__ __launch_bounds__(64) void gather_attn_kernel(GatherParams p) {
 
 // One wave per (sequence, head). Lanes hold the (m, l) of 64 splits at a time (all
 // loaded at once): pass 1 reduces the global max, pass 2 forms each split's weight in
-// its lane and broadcasts it while every lane streams its two dims of the partials,
-// 8 splits in flight (up to 32 splits: all partials requested up front instead). The
+// its lane and broadcasts it while every lane streams its two dims of the partials (up to
+// 32 splits: all partials requested up front instead). The
 // order of the sum is fixed, so the result is deterministic.
 template <class E>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part_o,
@@ -347,7 +347,6 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     }
     L += wave_sum_xor(w * l, 1);
     const int cnt = min(64, nsplit - s0);
-#pragma unroll 8
     for (int k = 0; k < cnt; ++k) {
       const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
       const float2 o = *reinterpret_cast<const float2*>(

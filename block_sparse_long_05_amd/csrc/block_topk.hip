@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
     uint32_t lb = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = lb | (1u << bit);
-      if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
+      if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
     }
     // b > K valid blocks sit in at least K lanes, so LB > 0 and padding keys never pass
     int n = 0;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
   uint32_t lb = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = lb | (1u << bit);
-    if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
+    if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
   }
   // 2. compact the candidates (ascending block order).
   int n = 0;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * kLongWaves) void block_topk_long_kernel(
     uint32_t lb = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = lb | (1u << bit);
-      if (__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
+      if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
     }
     uint32_t* ck = seg_key[wave];
     int32_t* ci = seg_idx[wave];
