@@ -94,6 +94,21 @@ def test_prefill_chunked_rows(algo, T, G, Hpg, top_k, q0, qn):
     assert np.isnan(lse[:q0]).all() and np.isnan(lse[q0 + qn:]).all()
 
 
+@pytest.mark.parametrize("algo", ["query_centric", "auto"])
+def test_prefill_topk_64(algo):
+    """The largest top_k (64): 64-slot lists and 64-bit per-token masks in the query-tile
+    kernel; rows with fewer visible blocks than k and rows that fill all 64 slots, checked
+    on a sample of rows."""
+    T, G, Hpg, d_idx, top_k = 8800, 1, 4, 64, 64
+    x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype="bf16", seed=64, planted_per_group=2)
+    print(f"prefill top_k 64 T={T} {algo}", flush=True)
+    out, idx, bs = _run_prefill(x, top_k, algo=algo)
+    rows = np.concatenate([np.arange(0, 8800, 97), np.arange(8500, 8800, 7)])
+    res = _oracle_prefill(("topk64", T), x, top_k, rows=rows)
+    parity.check_prefill(x, rows, out, idx, bs, res, top_k, label="k=64",
+                         lse_gpu=_LAST_LSE["lse"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_all_blocks_equals_dense(dtype):
     """top_k >= number of blocks: sparse prefill == the oracle's dense causal attention,
@@ -195,6 +210,7 @@ DECODE_CASES = [
     (2, 2000, [2000, 1280], 2, 3, 64, 4, "f32", 0),
     (4, 1000, [1000, 999, 129, 128], 4, 16, 128, 3, "bf16", 2),
     (2, 5000, [5000, 3333], 4, 8, 128, 40, "bf16", 4),  # top_k 40; 27 blocks < k: all kept
+    (1, 9000, [9000], 2, 4, 128, 64, "bf16", 3),         # the largest top_k: 64 of 71 blocks
 ]
 
 
