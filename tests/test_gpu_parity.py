@@ -58,6 +58,7 @@ PREFILL_CASES = [
     (640, 3, 1, 64, 3, "bf16", 0),      # one head per group, G = 3
     (1200, 2, 3, 128, 8, "bf16", 2),    # 3 heads: rows 30, 31 of every row tile unused
     (3500, 2, 2, 128, 24, "bf16", 3),   # top_k 24 > 16: the two-step index branch, wide lists
+    (700, 64, 1, 64, 3, "bf16", 1),     # the most groups the ABI allows
 ]
 
 
@@ -211,6 +212,7 @@ DECODE_CASES = [
     (4, 1000, [1000, 999, 129, 128], 4, 16, 128, 3, "bf16", 2),
     (2, 5000, [5000, 3333], 4, 8, 128, 40, "bf16", 4),  # top_k 40; 27 blocks < k: all kept
     (1, 9000, [9000], 2, 4, 128, 64, "bf16", 3),         # the largest top_k: 64 of 71 blocks
+    (2, 2000, [2000, 1500], 20, 2, 128, 4, "bf16", 2),   # G > 16: the general scan kernel
 ]
 
 
