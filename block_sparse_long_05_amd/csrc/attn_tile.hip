@@ -946,10 +946,13 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
 // bf16 form: 8 waves with one row tile each (a query tile is 8 row tiles), one workgroup
 // per CU with the shared blocks double-buffered in LDS: block j + 1 is loaded (K and V
 // row-major, by direct global->LDS loads) while block j is used; PV reads V through the
-// LDS transpose read. Q stays in registers across the shared blocks. A
-// row's running maximum is raised only when a new score exceeds it by more than 8 (log2
-// units), so the accumulator is rescaled rarely and every exponential stays below 2^8;
-// the final division by the row sum makes the result the same up to rounding.
+// LDS transpose read. Q stays in registers across the shared blocks. A block's four S
+// tiles and their maximum come first; a row's running maximum is raised only when that
+// block maximum exceeds it by more than 8 (log2 units), so the accumulator is rescaled
+// rarely and every exponential stays below 2^8; the final division by the row sum makes the
+// result the same up to rounding. A block every row of a wave sees whole skips the per-score
+// mask. The tile's kept entries are classified by all threads at once (LDS atomic ORs into
+// per-token masks), and each lane folds in its own rare partials through buffer views.
 template <int KMAX>
 __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
