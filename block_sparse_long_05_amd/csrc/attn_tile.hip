@@ -219,6 +219,82 @@ __global__ void kv_scatter_kernel(const int32_t* __restrict__ block_idx, int64_t
   }
 }
 
+// The same count and scatter with the per-block sums taken in LDS first: one workgroup per
+// (chunk of query rows, group) counts its entries per block with LDS atomics, then adds each
+// nonzero count to the (stripe, bucket) counter with one global atomic (stripe = chunk), so
+// a popular block costs one global atomic per chunk instead of one per entry. The scatter
+// reserves each block's range the same way, then walks its entries again and takes each
+// position from an LDS atomic on the reserved base. Used when the nblk counters and the
+// chunk's shared lists fit in LDS; the order of entries inside a bucket is arbitrary, as
+// with the kernels above. A chunk starts at a multiple of QT rows, so its tiles are whole.
+constexpr int kRiThreads = 512;
+constexpr int kRiLdsBytes = 64 * 1024;
+
+template <bool kScatter>
+__global__ __launch_bounds__(kRiThreads) void kv_index_lds_kernel(
+    const int32_t* __restrict__ block_idx, int64_t q_count, int G, int top_k, int64_t q_begin,
+    int nblk, const int32_t* __restrict__ shared, int QT, int rows, int32_t* __restrict__ ctr,
+    int32_t* __restrict__ sorted) {
+  extern __shared__ int32_t cnt[];  // nblk counters, then the shared lists of the chunk's tiles
+  const int tid = threadIdx.x;
+  // workgroups are dealt to the 8 XCDs in turn: renumber them so that the G groups of a chunk
+  // (whose ids share cache lines) run on one XCD and share its L2
+  unsigned wg = blockIdx.x;
+  if ((gridDim.x & 7u) == 0) wg = (wg & 7u) * (gridDim.x >> 3) + (wg >> 3);
+  const int g = (int)(wg % G);
+  const int64_t chunk = wg / G;
+  const int64_t i_lo = chunk * rows;
+  const int ntok = (int)min((int64_t)rows, q_count - i_lo);
+  const int64_t nb = (int64_t)G * nblk;
+  int32_t* gctr = ctr + (chunk % kStripes) * nb + (int64_t)g * nblk;
+  int32_t* sl = cnt + nblk;
+  const int ntl = shared != nullptr ? (ntok + QT - 1) / QT : 0;
+  for (int c = tid; c < nblk; c += kRiThreads) cnt[c] = 0;
+  for (int x = tid; x < ntl * top_k; x += kRiThreads) {
+    const int tl = x / top_k;
+    sl[x] = shared[((i_lo / QT + tl) * G + g) * top_k + (x - tl * top_k)];
+  }
+  __syncthreads();
+  const int ne = ntok * top_k;
+  const int t_lo = (int)(q_begin + i_lo);  // < 2^30
+  // block of entry e of the chunk, -1 when it does not go through the reverse index
+  auto bucket = [&](int e, int64_t* id) {
+    const int tok = e / top_k;
+    *id = ((i_lo + tok) * G + g) * top_k + (e - tok * top_k);
+    const int c = block_idx[*id];
+    if (c < 0 || c > (t_lo + tok) / kBlock) return -1;
+    if (shared != nullptr) {
+      const int32_t* l = sl + (tok / QT) * top_k;  // ascending, -1 padded
+      for (int j = 0; j < top_k; ++j) {
+        const int v = l[j];
+        if (v < 0 || v > c) break;
+        if (v == c) return -1;
+      }
+    }
+    return c;
+  };
+  for (int e = tid; e < ne; e += kRiThreads) {
+    int64_t id;
+    const int c = bucket(e, &id);
+    if (c >= 0) atomicAdd(&cnt[c], 1);
+  }
+  __syncthreads();
+  for (int c = tid; c < nblk; c += kRiThreads) {
+    const int n = cnt[c];
+    if (n > 0) {
+      const int base = atomicAdd(&gctr[c], n);
+      if (kScatter) cnt[c] = base;
+    }
+  }
+  if (!kScatter) return;
+  __syncthreads();
+  for (int e = tid; e < ne; e += kRiThreads) {
+    int64_t id;
+    const int c = bucket(e, &id);
+    if (c >= 0) sorted[atomicAdd(&cnt[c], 1)] = (int32_t)id;
+  }
+}
+
 // ---- the tile kernel ---------------------------------------------------------------------
 template <class E>
 struct TileOps;
@@ -1348,14 +1424,35 @@ void launch_reverse_index(const int32_t* block_idx, int64_t n_entries, int G, in
   const int64_t ncnt = nb * kStripes;
   hipLaunchKernelGGL(kv_zero_kernel, dim3((unsigned)std::min<int64_t>((ncnt + 255) / 256, 4096)),
                      dim3(256), 0, st, count, ncnt);
-  hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, shared, QT, count);
+  // LDS-aggregated form: about 512 workgroups, each over a whole number of query tiles, as
+  // long as the nblk counters and the chunk's shared lists fit in LDS
+  const int64_t q_count = n_entries / ((int64_t)G * top_k);
+  const int64_t per_g = std::max<int64_t>(1, 512 / G);
+  int64_t rows = ((q_count + per_g - 1) / per_g + QT - 1) / QT * QT;
+  if (shared != nullptr)
+    rows = std::min<int64_t>(rows, std::max<int64_t>(1, 4096 / top_k) * QT);
+  const int64_t ntl = shared != nullptr ? rows / QT : 0;
+  const size_t lds = (size_t)(nblk + ntl * top_k) * 4;
+  const bool lds_path = q_count > 0 && lds <= (size_t)kRiLdsBytes && rows < (int64_t(1) << 30);
+  const int64_t nchunk = lds_path ? (q_count + rows - 1) / rows : 0;
+  if (lds_path)
+    hipLaunchKernelGGL(kv_index_lds_kernel<false>, dim3((unsigned)(nchunk * G)),
+                       dim3(kRiThreads), lds, st, block_idx, q_count, G, top_k, q_begin, nblk,
+                       shared, QT, (int)rows, count, nullptr);
+  else
+    hipLaunchKernelGGL(kv_count_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
+                       top_k, q_begin, nblk, shared, QT, count);
   const unsigned grid_b = (unsigned)std::min<int64_t>((nb + 255) / 256, 65536);
   hipLaunchKernelGGL(kv_bucket_total_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset);
   launch_exclusive_scan(offset, nb, st);
   hipLaunchKernelGGL(kv_cursor_kernel, dim3(grid_b), dim3(256), 0, st, count, nb, offset, cursor);
-  hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries, G,
-                     top_k, q_begin, nblk, shared, QT, cursor, sorted);
+  if (lds_path)
+    hipLaunchKernelGGL(kv_index_lds_kernel<true>, dim3((unsigned)(nchunk * G)),
+                       dim3(kRiThreads), lds, st, block_idx, q_count, G, top_k, q_begin, nblk,
+                       shared, QT, (int)rows, cursor, sorted);
+  else
+    hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_e), dim3(256), 0, st, block_idx, n_entries,
+                       G, top_k, q_begin, nblk, shared, QT, cursor, sorted);
 }
 
 size_t kv_workspace_bytes(int bf16, int64_t q_count, int G, int Hpg, int top_k, int nblk) {
