@@ -4,7 +4,8 @@ times, on outputs the oracle can compute one by one (sampled query rows / sequen
 Workloads: decode of 4 sequences x 131072 cached tokens (all rows checked), decode of
 8 x 1,048,576 (two sequences checked), causal prefill of 131072 tokens (sampled
 32-token slices) and of 1,048,576 tokens (sampled 8-token slices), the index-branch KL
-loss at 131072 tokens. All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
+loss at 131072 tokens, and the tail rows of a 2,097,152-token sequence, long enough that the
+reverse index takes its per-entry atomic form. All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
 index dim 128, 128-token blocks, top_k 16, planted blocks as in the benchmark.
 """
 
@@ -149,4 +150,39 @@ def test_prefill_1m_sampled_rows():
         got_idx = idx[lo:lo + 8].cpu().numpy()
         info = parity.check_prefill(host, rows, got_out, got_idx, None, res, k, q_begin=lo,
                                     out_offset=lo, label=f"1M rows {lo}")
+        print(lo, info, flush=True)
+
+
+def test_prefill_reverse_index_beyond_lds_counters():
+    """A 2,097,152-token sequence (16384 blocks): the per-block counters of the reverse index and a
+    chunk's shared lists no longer fit in 64 KiB of LDS, so the attention sorts its rare entries
+    with one device-scope atomic per entry. The last 1000 query rows (a ragged query tile at one
+    head per group) run the fused index branch and the attention; sampled rows against the oracle."""
+    T, G, Hpg, k = 1 << 21, 1, 1, 16
+    q_count = 1000
+    q_begin = T - q_count
+    # 8 planted blocks (shared by the query tiles) + the local block + 7 independent choices
+    # per row (the rare entries that go through the reverse index)
+    x = synth.prefill_inputs(T, G, Hpg, 128, 128, dtype="bf16", seed=77, planted_per_group=8,
+                             device="cuda")
+    p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=Hpg,
+                    index_dim=128, top_k=k, seq_len=T, q_begin=q_begin, q_count=q_count)
+    assert p.nblk * 4 >= 64 * 1024  # the per-block counters alone fill 64 KiB
+    idx = msa.alloc_block_idx(p)
+    msa.msa_index_topk(p, x["q_idx"], x["k_idx"], idx)
+    out = torch.empty_like(x["q"])
+    ws = msa.alloc_workspace(p, "sparse_attn_prefill")
+    msa.msa_sparse_attn_prefill(p, x["q"], x["k"], x["v"], idx, out, ws)
+    torch.cuda.synchronize()
+    print("prefill 2M tail ran", flush=True)
+    del ws
+    host = {kk: x[kk].cpu() for kk in ("q", "k", "v", "q_idx", "k_idx")}
+    for lo in (q_begin, q_begin + 509, T - 8):
+        rows = np.arange(lo, lo + 8)
+        res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], k,
+                          rows=rows)
+        got_out = out[lo:lo + 8].float().cpu().numpy()
+        got_idx = idx[lo - q_begin:lo - q_begin + 8].cpu().numpy()
+        info = parity.check_prefill(host, rows, got_out, got_idx, None, res, k, q_begin=lo,
+                                    out_offset=lo, label=f"2M rows {lo}")
         print(lo, info, flush=True)
