@@ -6,7 +6,8 @@ Workloads: decode of 4 sequences x 131072 cached tokens (all rows checked), deco
 32-token slices) and of 1,048,576 tokens (sampled 8-token slices), the index-branch KL
 loss at 131072 tokens, and the tail rows of a 2,097,152-token sequence, long enough that the
 reverse index takes its per-entry atomic form. All bf16 with 8 KV heads x 8 query heads per group, head_dim 128,
-index dim 128, 128-token blocks, top_k 16, planted blocks as in the benchmark.
+index dim 128, 128-token blocks, top_k 16, planted blocks as in the benchmark (the 2M tail:
+one KV head with one query head, to keep its inputs small).
 """
 
 import numpy as np
