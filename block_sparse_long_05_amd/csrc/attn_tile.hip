@@ -11,7 +11,8 @@
 //   1. kv_classify_kernel: per query tile (a few consecutive tokens) and group, the
 //      blocks kept by at least half of the tile's tokens form the tile's shared list;
 //   2. reverse index of the other ("rare") kept entries: a counting sort by KV block
-//      (group g, block c) - count, exclusive scan, scatter;
+//      (group g, block c) - count, exclusive scan, scatter, with each chunk of rows
+//      summing its per-block counts in LDS before one global atomic per block;
 //   3. kv_attn_kernel: the sorted rare entries are cut into fixed tiles of 256 entries
 //      (load balance independent of how popular a block is). Each tile walks its runs
 //      of equal (g, c): the block's K and V (transposed) are staged in LDS once and
