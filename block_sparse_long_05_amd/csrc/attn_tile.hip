@@ -21,9 +21,9 @@
 //      the block; it writes a partial (o / l, m, l);
 //   4. qtile_attn kernels: per (query tile, group) the shared blocks are staged in LDS
 //      one after another and every row of the tile runs an online softmax over those it
-//      keeps (others masked); the row then folds in its rare partials with a
-//      log-sum-exp combine in slot order (deterministic; no atomics touch values) and
-//      writes the output.
+//      keeps (others masked); the row also folds in its rare partials with a log-sum-exp
+//      combine in slot order (deterministic; no atomics touch values; the bf16 kernel
+//      folds them first, while its first shared block is staged) and writes the output.
 //
 // MFMA orientation: S^T = K . Q^T so that a lane owns one query row and holds 16 of
 // its keys per 32-key tile; the softmax reductions are in-lane plus one exchange
@@ -1029,7 +1029,9 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
 // rarely and every exponential stays below 2^8; the final division by the row sum makes the
 // result the same up to rounding. A block every row of a wave sees whole skips the per-score
 // mask. The tile's kept entries are classified by all threads at once (LDS atomic ORs into
-// per-token masks), and each lane folds in its own rare partials through buffer views.
+// per-token masks), and each lane folds in its own rare partials through buffer views,
+// before the shared blocks: their loads overlap the first block's staging, and the partials'
+// maximum starts the row's running maximum.
 template <int KMAX>
 __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -1106,6 +1108,74 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const int c0 = __builtin_amdgcn_readfirstlane(sl[0]);
     k_block_dma_s<512>(K, g, c0, seq_len, Kb0, wv, dma_lane_off<false>(lane), tid);
     k_block_dma_s<512, true>(V, g, c0, seq_len, Vb0, wv, dma_lane_off<true>(lane), tid);
+  }
+  // Rare partials first, while the first shared block is being staged: pass 1 reads every
+  // rare slot's (m, l) to fix their maximum, which becomes the row's running maximum; pass 2
+  // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
+  // them: each load instruction covers whole cache lines). Each lane walks only its own
+  // rare slots, in slot order, so a wave iterates as often as its busiest token has rare
+  // slots. The partials are read through buffer views of the tile's entries (group g, 32-bit
+  // offsets); a lane with no slot left reads past the bound and gets zeros, so no load
+  // sits behind a branch. The shared blocks then continue the same online softmax.
+  if (__ballot(myrare != 0)) {
+    const int64_t ebase = (i0 * G + g) * top_k;
+    const uint32_t span = (uint32_t)((int64_t)(ntok - 1) * G * top_k + top_k);  // < 2^20
+    const __amdgpu_buffer_rsrc_t v_ml = buffer_view(part_ml + ebase * Hpg * 2, span * Hpg * 8);
+    const __amdgpu_buffer_rsrc_t v_o =
+        buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
+    const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
+    // slots whose loads are issued together: (m, l) pairs in pass 1, partials in pass 2
+    constexpr int kMlPer = 4, kPartPer = 2;
+    float M = m_run;
+    for (uint64_t rem = myrare; __ballot(rem != 0);) {
+      float x[kMlPer];
+      bool hs[kMlPer];
+#pragma unroll
+      for (int k2 = 0; k2 < kMlPer; ++k2) {
+        hs[k2] = rem != 0;
+        const uint32_t s2 = (uint32_t)__builtin_ctzll(rem | (1ull << 63));
+        rem &= rem - 1ull;
+        const uint32_t off = hs[k2] ? ((tok_e + s2) * Hpg + h) * 8 : kBufNone;
+        x[k2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v_ml, off, 0, 0));
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < kMlPer; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
+    }
+    m_run = M;  // finite for a lane with a rare slot, -inf otherwise (no score yet)
+    const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
+    for (uint64_t rem = myrare; __ballot(rem != 0);) {
+      float2 ml[kPartPer];
+      u32x4 w4[kPartPer][8];
+      bool hs[kPartPer];
+#pragma unroll
+      for (int k2 = 0; k2 < kPartPer; ++k2) {
+        hs[k2] = rem != 0;
+        const uint32_t ent = tok_e + (uint32_t)__builtin_ctzll(rem | (1ull << 63));
+        rem &= rem - 1ull;
+        ml[k2] = __builtin_bit_cast(
+            float2, __builtin_amdgcn_raw_buffer_load_b64(
+                        v_ml, hs[k2] ? (ent * Hpg + h) * 8 : kBufNone, 0, 0));
+        const uint32_t ob = hs[k2] ? ent * Hpg * kHeadDim * 2 + lane_b : kBufNone;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          w4[k2][i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_o, ob + i * 32 * Hpg, 0, 0));
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < kPartPer; ++k2) {
+        const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - M) : 0.f;
+        l_run += w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j2 = 0; j2 < 8; ++j2) {
+            const uint32_t bits =
+                j2 & 1 ? w4[k2][i][j2 >> 1] >> 16 : w4[k2][i][j2 >> 1] & 0xffffu;
+            const int r = 4 * (2 * (i & 1) + (j2 >> 2)) + (j2 & 3);
+            o[i >> 1][r] = fmaf(w, bf16_bits_to_f32(bits), o[i >> 1][r]);
+          }
+      }
+    }
   }
   auto shared_block = [&](int j, const uint8_t* Kc, const uint8_t* Vc, uint8_t* Kn, uint8_t* Vn) {
     const int c = __builtin_amdgcn_readfirstlane(sl[j]);  // uniform: scalar staging base
@@ -1194,84 +1264,10 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     if (j + 1 < ns) shared_block(j + 1, Kb1, Vb1, Kb0, Vb0);
   }
 
-  // Rare partials: pass 1 reads every rare slot's (m, l) to fix the final maximum, pass 2
-  // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
-  // them: each load instruction covers whole cache lines). Each lane walks only its own
-  // rare slots, in slot order, so a wave iterates as often as its busiest token has rare
-  // slots. The partials are read through buffer views of the tile's entries (group g, 32-bit
-  // offsets); a lane with no slot left reads past the bound and gets zeros, so no load
-  // sits behind a branch.
-  float m_fin = m_run;  // the reference maximum of l_run once the partials are in
-  if (__ballot(myrare != 0)) {
-    const int64_t ebase = (i0 * G + g) * top_k;
-    const uint32_t span = (uint32_t)((int64_t)(ntok - 1) * G * top_k + top_k);  // < 2^20
-    const __amdgpu_buffer_rsrc_t v_ml = buffer_view(part_ml + ebase * Hpg * 2, span * Hpg * 8);
-    const __amdgpu_buffer_rsrc_t v_o =
-        buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
-    const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
-    // slots whose loads are issued together: (m, l) pairs in pass 1, partials in pass 2
-    constexpr int kMlPer = 4, kPartPer = 2;
-    float M = m_run;
-    for (uint64_t rem = myrare; __ballot(rem != 0);) {
-      float x[kMlPer];
-      bool hs[kMlPer];
-#pragma unroll
-      for (int k2 = 0; k2 < kMlPer; ++k2) {
-        hs[k2] = rem != 0;
-        const uint32_t s2 = (uint32_t)__builtin_ctzll(rem | (1ull << 63));
-        rem &= rem - 1ull;
-        const uint32_t off = hs[k2] ? ((tok_e + s2) * Hpg + h) * 8 : kBufNone;
-        x[k2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v_ml, off, 0, 0));
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < kMlPer; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
-    }
-    m_fin = M;
-    const float a = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
-    l_run *= a;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= a;
-    const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
-    for (uint64_t rem = myrare; __ballot(rem != 0);) {
-      float2 ml[kPartPer];
-      u32x4 w4[kPartPer][8];
-      bool hs[kPartPer];
-#pragma unroll
-      for (int k2 = 0; k2 < kPartPer; ++k2) {
-        hs[k2] = rem != 0;
-        const uint32_t ent = tok_e + (uint32_t)__builtin_ctzll(rem | (1ull << 63));
-        rem &= rem - 1ull;
-        ml[k2] = __builtin_bit_cast(
-            float2, __builtin_amdgcn_raw_buffer_load_b64(
-                        v_ml, hs[k2] ? (ent * Hpg + h) * 8 : kBufNone, 0, 0));
-        const uint32_t ob = hs[k2] ? ent * Hpg * kHeadDim * 2 + lane_b : kBufNone;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          w4[k2][i] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_o, ob + i * 32 * Hpg, 0, 0));
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < kPartPer; ++k2) {
-        const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - M) : 0.f;
-        l_run += w;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j2 = 0; j2 < 8; ++j2) {
-            const uint32_t bits =
-                j2 & 1 ? w4[k2][i][j2 >> 1] >> 16 : w4[k2][i][j2 >> 1] & 0xffffu;
-            const int r = 4 * (2 * (i & 1) + (j2 >> 2)) + (j2 & 3);
-            o[i >> 1][r] = fmaf(w, bf16_bits_to_f32(bits), o[i >> 1][r]);
-          }
-      }
-    }
-  }
   if (ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (lse != nullptr && q == 0)
-      lse[t * Hq + (int64_t)g * Hpg + h] = l_run > 0.f ? (m_fin + log2f(l_run)) * kLn2 : -INFINITY;
+      lse[t * Hq + (int64_t)g * Hpg + h] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     uint16_t* dst = out + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
