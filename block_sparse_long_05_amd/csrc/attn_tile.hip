@@ -1030,8 +1030,8 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
 // result the same up to rounding. A block every row of a wave sees whole skips the per-score
 // mask. The tile's kept entries are classified by all threads at once (LDS atomic ORs into
 // per-token masks), and each lane folds in its own rare partials through buffer views,
-// before the shared blocks: their loads overlap the first block's staging, and the partials'
-// maximum starts the row's running maximum.
+// before the shared blocks, in one online pass with the same lazy maximum: their loads
+// overlap the first block's staging.
 template <int KMAX>
 __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -1109,14 +1109,14 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     k_block_dma_s<512>(K, g, c0, seq_len, Kb0, wv, dma_lane_off<false>(lane), tid);
     k_block_dma_s<512, true>(V, g, c0, seq_len, Vb0, wv, dma_lane_off<true>(lane), tid);
   }
-  // Rare partials first, while the first shared block is being staged: pass 1 reads every
-  // rare slot's (m, l) to fix their maximum, which becomes the row's running maximum; pass 2
-  // adds the weighted partials (lane-interleaved entry blocks, as the tile kernel wrote
-  // them: each load instruction covers whole cache lines). Each lane walks only its own
+  // Rare partials first, while the first shared block is being staged: one pass reads each
+  // rare slot's (m, l) and partial (lane-interleaved entry blocks, as the tile kernel wrote
+  // them: each load instruction covers whole cache lines) and merges it into the row's
+  // online softmax, which the shared blocks then continue. Each lane walks only its own
   // rare slots, in slot order, so a wave iterates as often as its busiest token has rare
   // slots. The partials are read through buffer views of the tile's entries (group g, 32-bit
   // offsets); a lane with no slot left reads past the bound and gets zeros, so no load
-  // sits behind a branch. The shared blocks then continue the same online softmax.
+  // sits behind a branch.
   if (__ballot(myrare != 0)) {
     const int64_t ebase = (i0 * G + g) * top_k;
     const uint32_t span = (uint32_t)((int64_t)(ntok - 1) * G * top_k + top_k);  // < 2^20
@@ -1124,24 +1124,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const __amdgpu_buffer_rsrc_t v_o =
         buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
     const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
-    // slots whose loads are issued together: (m, l) pairs in pass 1, partials in pass 2
-    constexpr int kMlPer = 4, kPartPer = 2;
-    float M = m_run;
-    for (uint64_t rem = myrare; __ballot(rem != 0);) {
-      float x[kMlPer];
-      bool hs[kMlPer];
-#pragma unroll
-      for (int k2 = 0; k2 < kMlPer; ++k2) {
-        hs[k2] = rem != 0;
-        const uint32_t s2 = (uint32_t)__builtin_ctzll(rem | (1ull << 63));
-        rem &= rem - 1ull;
-        const uint32_t off = hs[k2] ? ((tok_e + s2) * Hpg + h) * 8 : kBufNone;
-        x[k2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v_ml, off, 0, 0));
-      }
-#pragma unroll
-      for (int k2 = 0; k2 < kMlPer; ++k2) M = hs[k2] ? fmaxf(M, x[k2]) : M;
-    }
-    m_run = M;  // finite for a lane with a rare slot, -inf otherwise (no score yet)
+    // slots whose (m, l) and partial loads are issued together
+    constexpr int kPartPer = 2;
     const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
     for (uint64_t rem = myrare; __ballot(rem != 0);) {
       float2 ml[kPartPer];
@@ -1161,9 +1145,25 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
           w4[k2][i] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_o, ob + i * 32 * Hpg, 0, 0));
       }
+      // online merge with the lazy maximum of the block loop: the running maximum (-inf
+      // before the lane's first slot) is raised only when a partial's maximum exceeds it by
+      // more than 8, so every weight below stays under 2^8 times its l
+      float mr = -INFINITY;
+#pragma unroll
+      for (int k2 = 0; k2 < kPartPer; ++k2) mr = hs[k2] ? fmaxf(mr, ml[k2].x) : mr;
+      const bool raise = mr > m_run + 8.f;
+      if (__ballot(raise)) {
+        const float alpha = raise ? (m_run == -INFINITY ? 0.f : fast_exp2(m_run - mr)) : 1.f;
+        m_run = raise ? mr : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
 #pragma unroll
       for (int k2 = 0; k2 < kPartPer; ++k2) {
-        const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - M) : 0.f;
+        const float w = hs[k2] ? ml[k2].y * fast_exp2(ml[k2].x - m_run) : 0.f;
         l_run += w;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
