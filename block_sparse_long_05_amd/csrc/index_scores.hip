@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_prefill_kernel(
     tk[i] = 0u;  // below the key of every finite float
     ti[i] = -1;
   }
-  if (cmax >= top_k) {  // some row of the workgroup ranks blocks
+  if (cmax >= top_k && top_k > 1) {  // some row of the workgroup ranks blocks
     u32x4 qop[RT][C::kSteps];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {

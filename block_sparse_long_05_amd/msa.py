@@ -263,6 +263,69 @@ def alloc_block_idx(p: Problem, device="cuda") -> torch.Tensor:
     return torch.empty((p.rows, p.num_groups, p.top_k), dtype=torch.int32, device=device)
 
 
+# ---- input checks of the high-level helpers ---------------------------------------------
+# The C ABI sees only pointers, so it cannot tell a mismatched shape or dtype from a valid
+# one; the helpers below check what their arguments imply before any launch.
+
+_DT = {torch.float32: "f32", torch.bfloat16: "bf16"}
+
+
+def _expect(t, name, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def check_prefill_inputs(x: dict) -> tuple:
+    """Validates q [T, Hq, 128], k, v [G, T, 128], q_idx [T, G, d], k_idx [T, d] (one dtype,
+    fp32 or bf16, Hq divisible by G); returns (T, G, Hpg, d, dtype name)."""
+    q = x["q"]
+    if q.dim() != 3 or q.dtype not in _DT:
+        raise ValueError("q must be [T, Hq, D] fp32 or bf16")
+    T, Hq, D = q.shape
+    if x["k"].dim() != 3:
+        raise ValueError("k must be [G, T, D]")
+    G = x["k"].shape[0]
+    if G < 1 or Hq % G != 0:
+        raise ValueError(f"Hq = {Hq} query heads are not a multiple of G = {G} groups")
+    d = x["q_idx"].shape[-1]
+    _expect(x["k"], "k", (G, T, D), q.dtype)
+    _expect(x["v"], "v", (G, T, D), q.dtype)
+    _expect(x["q_idx"], "q_idx", (T, G, d), q.dtype)
+    _expect(x["k_idx"], "k_idx", (T, d), q.dtype)
+    return T, G, Hq // G, d, _DT[q.dtype]
+
+
+def check_decode_inputs(x: dict) -> tuple:
+    """Validates q [B, Hq, 128], k_cache, v_cache [B, G, max_len, 128], q_idx [B, G, d],
+    k_idx [B, max_len, d] (one dtype), seq_lens int32 [B]; returns (B, G, Hpg, d, max_len,
+    dtype name)."""
+    q = x["q"]
+    if q.dim() != 3 or q.dtype not in _DT:
+        raise ValueError("q must be [B, Hq, D] fp32 or bf16")
+    B, Hq, D = q.shape
+    if x["k_cache"].dim() != 4:
+        raise ValueError("k_cache must be [B, G, max_len, D]")
+    G, L = x["k_cache"].shape[1], x["k_cache"].shape[2]
+    if G < 1 or Hq % G != 0:
+        raise ValueError(f"Hq = {Hq} query heads are not a multiple of G = {G} groups")
+    d = x["q_idx"].shape[-1]
+    _expect(x["k_cache"], "k_cache", (B, G, L, D), q.dtype)
+    _expect(x["v_cache"], "v_cache", (B, G, L, D), q.dtype)
+    _expect(x["q_idx"], "q_idx", (B, G, d), q.dtype)
+    _expect(x["k_idx"], "k_idx", (B, L, d), q.dtype)
+    _expect(x["seq_lens"], "seq_lens", (B,), torch.int32)
+    return B, G, Hq // G, d, L, _DT[q.dtype]
+
+
+def _check_out(t, name, shape, dtype):
+    if t is not None:
+        _expect(t, name, shape, dtype)
+
+
 # ---- the whole hot path, as a chain of the C calls ------------------------------------------
 
 def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None,
@@ -274,15 +337,18 @@ def prefill(x: dict, top_k: int, q_begin: int = 0, q_count: Optional[int] = None
     index branch as msa_index_topk (no block scores; block_scores is returned as None).
     Returns (out, block_idx, block_scores)."""
     q = x["q"]
-    T, Hq, D = q.shape
-    G = x["k"].shape[0]
+    T, G, Hpg, d, dt = check_prefill_inputs(x)
     if q_count is None:
         q_count = T - q_begin
-    p = Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="prefill",
-                num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
-                top_k=top_k, head_dim=D, seq_len=T, q_begin=q_begin, q_count=q_count, algo=algo)
+    p = Problem(dtype=dt, mode="prefill", num_groups=G, heads_per_group=Hpg, index_dim=d,
+                top_k=top_k, head_dim=q.shape[2], seq_len=T, q_begin=q_begin, q_count=q_count,
+                algo=algo)
     if index not in ("separate", "fused"):
         raise ValueError(f"index must be 'separate' or 'fused', not {index!r}")
+    _check_out(out, "out", q.shape, q.dtype)
+    _check_out(lse, "lse", q.shape[:2], torch.float32)
+    _check_out(block_idx, "block_idx", (q_count, G, top_k), torch.int32)
+    _check_out(block_scores, "block_scores", (q_count, G, p.nblk), torch.float32)
     if out is None:
         out = torch.empty_like(q)
     if block_idx is None:
@@ -309,13 +375,14 @@ def index_kl(x: dict, block_idx, top_k: int, index_scale: float, q_begin: int = 
     dk_idx (fp32 [T, 128]) is accumulated into; a zeroed one is made when it is None.
     Returns (loss [q_count, G], dq_idx [q_count, G, 128], dk_idx)."""
     q = x["q"]
-    T, Hq, D = q.shape
-    G = x["k"].shape[0]
+    T, G, Hpg, d, dt = check_prefill_inputs(dict(x, v=x["k"]))
     if q_count is None:
         q_count = T - q_begin
-    p = Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="prefill",
-                num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
-                top_k=top_k, head_dim=D, seq_len=T, q_begin=q_begin, q_count=q_count)
+    p = Problem(dtype=dt, mode="prefill", num_groups=G, heads_per_group=Hpg, index_dim=d,
+                top_k=top_k, head_dim=q.shape[2], seq_len=T, q_begin=q_begin, q_count=q_count)
+    _expect(block_idx, "block_idx", (q_count, G, top_k), torch.int32)
+    _check_out(dk_idx, "dk_idx", (T, d), torch.float32)
+    _check_out(main_lse, "main_lse", q.shape[:2], torch.float32)
     loss = torch.empty((q_count, G), dtype=torch.float32, device=q.device)
     dq = torch.empty((q_count, G, x["q_idx"].shape[-1]), dtype=torch.float32, device=q.device)
     if dk_idx is None:
@@ -329,12 +396,9 @@ def index_kl(x: dict, block_idx, top_k: int, index_scale: float, q_begin: int = 
 
 def decode_problem(x: dict, top_k: int) -> Problem:
     q = x["q"]
-    B, Hq, D = q.shape
-    G = x["k_cache"].shape[1]
-    return Problem(dtype="bf16" if q.dtype == torch.bfloat16 else "f32", mode="decode",
-                   num_groups=G, heads_per_group=Hq // G, index_dim=x["q_idx"].shape[-1],
-                   top_k=top_k, head_dim=D, batch=B, max_len=x["k_cache"].shape[2],
-                   seq_lens=x["seq_lens"])
+    B, G, Hpg, d, L, dt = check_decode_inputs(x)
+    return Problem(dtype=dt, mode="decode", num_groups=G, heads_per_group=Hpg, index_dim=d,
+                   top_k=top_k, head_dim=q.shape[2], batch=B, max_len=L, seq_lens=x["seq_lens"])
 
 
 def decode(x: dict, top_k: int, out=None, block_scores=None, block_idx=None, workspace=None,
@@ -342,6 +406,9 @@ def decode(x: dict, top_k: int, out=None, block_scores=None, block_idx=None, wor
     """One MSA decode step: index scan -> top-k -> split-K sparse attention + combine.
     Returns (out, block_idx, block_scores)."""
     p = decode_problem(x, top_k)
+    _check_out(out, "out", x["q"].shape, x["q"].dtype)
+    _check_out(block_scores, "block_scores", (p.batch, p.num_groups, p.nblk), torch.float32)
+    _check_out(block_idx, "block_idx", (p.batch, p.num_groups, top_k), torch.int32)
     if out is None:
         out = torch.empty_like(x["q"])
     if block_scores is None:

@@ -436,8 +436,10 @@ def selection_array(sel, top_k: int) -> np.ndarray:
 
 def attend_on_selection(q_t, k_g, v_g, sel, t, block: int = BLOCK) -> np.ndarray:
     """Attention of one token's group heads over a given selection (for rows where
-    a device picked a different set on a declared near tie)."""
+    a device picked a different set on a declared near tie). Ids < 0 are padding; the
+    others must be distinct (a repeated id would count its block twice)."""
     q_t, k_g, v_g = as_f64(q_t), host(k_g), host(v_g)
     sel = [int(c) for c in sel if int(c) >= 0]
+    assert len(set(sel)) == len(sel), f"repeated block id in {sel}"
     j = visible_keys(sel, t, block)
     return attend(q_t, as_f64(k_g[j]), as_f64(v_g[j]), 1.0 / math.sqrt(q_t.shape[-1]))

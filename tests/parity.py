@@ -36,15 +36,59 @@ def check_block_scores(bs_gpu, oracle_scores, row_map, label=""):
     return worst
 
 
-def check_selection(idx_gpu, oracle_sel, near_tie, top_k, label=""):
-    """Returns the set of (i, g) rows whose selection differs (all near ties)."""
-    ref = orc.selection_array(oracle_sel, top_k)
+def validate_tie_selection(sel_row, scores, b, top_k, label=""):
+    """A device selection on a row the oracle declares a near tie must still be a valid
+    selection under the rule (researchpapers.dev summary, "Mechanism": the local block is
+    always kept; the others are the best-scoring earlier blocks), with only blocks whose
+    fp64 scores sit within the near-tie gap of the cut allowed to trade places:
+      * ids ascending and distinct, the local block b last, the others in [0, b), exactly
+        min(top_k, b + 1) of them, -1 after;
+      * every chosen earlier block scores >= r_k - gap and every unchosen earlier block
+        <= r_{k-1} + gap, where r_{k-1} >= r_k are the (k-1)-th and k-th best earlier
+        scores (the oracle's last kept and first dropped) and gap = 1e-5 * max(|r_{k-1}|,
+        |r_k|), the near-tie threshold."""
+    sel_row = np.asarray(sel_row).astype(np.int64)
+    n = min(top_k, b + 1)
+    ids, pad = sel_row[:n], sel_row[n:]
+    assert np.all(pad == -1), f"{label}: padding {pad.tolist()}"
+    assert np.all(np.diff(ids) > 0), f"{label}: ids not ascending/distinct {ids.tolist()}"
+    assert ids[-1] == b, f"{label}: local block {b} missing from {ids.tolist()}"
+    others = ids[:-1]
+    assert len(others) == 0 or (others.min() >= 0 and others.max() < b), (
+        f"{label}: ids outside [0, {b}) in {ids.tolist()}")
+    if b + 1 <= top_k:
+        return
+    scores = np.asarray(scores, dtype=np.float64)[:b] + 0.0
+    ranked = np.sort(scores)[::-1]
+    r_last, r_next = ranked[top_k - 2], ranked[top_k - 1]
+    gap = orc.NEAR_TIE_REL * max(abs(r_last), abs(r_next))
+    chosen = np.zeros(b, dtype=bool)
+    chosen[others] = True
+    assert np.all(scores[chosen] >= r_next - gap), (
+        f"{label}: a kept block scores {scores[chosen].min()} < cut {r_next}")
+    if (~chosen).any():
+        assert np.all(scores[~chosen] <= r_last + gap), (
+            f"{label}: a dropped block scores {scores[~chosen].max()} > cut {r_last}")
+
+
+def check_selection(idx_gpu, res, top_k, local_blocks, label=""):
+    """idx_gpu [R, G, top_k]: the device's ids for the R oracle rows of `res` (an oracle
+    prefill/decode result), local_blocks [R] the rows' local blocks. Rows must match the
+    oracle bit for bit unless the oracle declares a near tie; on such rows the device's
+    set must pass validate_tie_selection against the oracle's fp64 block scores.
+    Returns the set of (i, g) rows whose selection differs."""
+    ref = orc.selection_array(res["sel"], top_k)
     diff = np.any(idx_gpu != ref, axis=2)
-    bad = diff & ~near_tie
+    bad = diff & ~res["near_tie"]
     assert not bad.any(), (
         f"{label}: {int(bad.sum())} rows differ without a near tie, first "
         f"{np.argwhere(bad)[:5].tolist()}")
-    return {tuple(x) for x in np.argwhere(diff).tolist()}
+    differ = {tuple(x) for x in np.argwhere(diff).tolist()}
+    for (i, g) in differ:
+        b = int(local_blocks[i])
+        validate_tie_selection(idx_gpu[i, g], res["block_scores"][(i, g)], b, top_k,
+                               label=f"{label} row {i} group {g}")
+    return differ
 
 
 def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, out_offset=0,
@@ -57,7 +101,7 @@ def check_prefill(x, rows, out_gpu, idx_gpu, bs_gpu, res, top_k, q_begin=0, out_
     Hpg = x["q"].shape[1] // G
     rows = np.asarray(rows)
     idx_rows = idx_gpu[rows - q_begin]
-    differ = check_selection(idx_rows, res["sel"], res["near_tie"], top_k, label)
+    differ = check_selection(idx_rows, res, top_k, rows // orc.BLOCK, label)
     if bs_gpu is not None:
         check_block_scores(bs_gpu, res["block_scores"], lambda i: rows[i] - q_begin, label)
     got = out_gpu[rows - out_offset].astype(np.float64)
@@ -86,12 +130,12 @@ def check_decode(x, out_gpu, idx_gpu, bs_gpu, res, top_k, label=""):
     tol = OUT_TOL[dtype]
     G = x["k_cache"].shape[1]
     Hpg = x["q"].shape[1] // G
-    differ = check_selection(idx_gpu, res["sel"], res["near_tie"], top_k, label)
+    lens = x["seq_lens"].cpu().numpy()
+    differ = check_selection(idx_gpu, res, top_k, (lens - 1) // orc.BLOCK, label)
     if bs_gpu is not None:
         check_block_scores(bs_gpu, res["block_scores"], lambda i: i, label)
     got = out_gpu.astype(np.float64)
     ref = res["out"].copy()
-    lens = x["seq_lens"].cpu().numpy()
     for (b, g) in differ:
         hs = slice(g * Hpg, (g + 1) * Hpg)
         ref[b, hs] = orc.attend_on_selection(x["q"][b, hs], x["k_cache"][b, g],

@@ -254,3 +254,50 @@ def test_entry_count_limit_of_the_reverse_index():
     assert lib.msa_workspace_size(ctypes.byref(_prefill(algo="kv_centric", **under).c()),
                                   msa.ENTRY["sparse_attn_prefill"], ctypes.byref(n)) == msa.MSA_OK
     assert n.value > 0
+
+
+def test_python_helpers_reject_mismatched_inputs():
+    """The C ABI cannot see buffer sizes, so the high-level helpers check shapes and dtypes
+    before any launch: a mixed dtype, a head count that is not a multiple of the groups, or
+    a wrongly shaped tensor raises ValueError (the tensors here never reach the device)."""
+    import torch
+    T, G, Hpg, d = 256, 2, 3, 64
+
+    def pre(dtype=torch.bfloat16, **over):
+        x = dict(q=torch.zeros(T, G * Hpg, 128, dtype=dtype),
+                 k=torch.zeros(G, T, 128, dtype=dtype), v=torch.zeros(G, T, 128, dtype=dtype),
+                 q_idx=torch.zeros(T, G, d, dtype=dtype), k_idx=torch.zeros(T, d, dtype=dtype))
+        x.update(over)
+        return x
+
+    assert msa.check_prefill_inputs(pre()) == (T, G, Hpg, d, "bf16")
+    bad = [pre(k=torch.zeros(G, T, 128, dtype=torch.float32)),            # mixed dtype
+           pre(q=torch.zeros(T, 7, 128, dtype=torch.bfloat16)),             # 7 heads, 2 groups
+           pre(v=torch.zeros(G, T - 1, 128, dtype=torch.bfloat16)),         # short v
+           pre(q_idx=torch.zeros(T, G + 1, d, dtype=torch.bfloat16)),       # wrong groups
+           pre(k_idx=torch.zeros(T, 128, dtype=torch.bfloat16)),            # wrong index dim
+           pre(dtype=torch.float16)]                                         # unsupported dtype
+    for x in bad:
+        with pytest.raises(ValueError):
+            msa.prefill(x, 4)
+    with pytest.raises(ValueError):   # an output buffer of the wrong shape
+        msa.prefill(pre(), 4, block_idx=torch.zeros(T, G, 5, dtype=torch.int32))
+    B, L = 2, 512
+
+    def dec(**over):
+        dt = torch.bfloat16
+        x = dict(q=torch.zeros(B, G * Hpg, 128, dtype=dt),
+                 k_cache=torch.zeros(B, G, L, 128, dtype=dt),
+                 v_cache=torch.zeros(B, G, L, 128, dtype=dt),
+                 q_idx=torch.zeros(B, G, d, dtype=dt), k_idx=torch.zeros(B, L, d, dtype=dt),
+                 seq_lens=torch.full((B,), L, dtype=torch.int32))
+        x.update(over)
+        return x
+
+    assert msa.check_decode_inputs(dec()) == (B, G, Hpg, d, L, "bf16")
+    for x in [dec(k_idx=torch.zeros(B, L, d, dtype=torch.float32)),
+              dec(v_cache=torch.zeros(B, G, L // 2, 128, dtype=torch.bfloat16)),
+              dec(seq_lens=torch.full((B,), L, dtype=torch.int64)),
+              dec(q=torch.zeros(B, 5, 128, dtype=torch.bfloat16))]:
+        with pytest.raises(ValueError):
+            msa.decode(x, 4)

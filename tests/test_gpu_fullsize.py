@@ -107,7 +107,7 @@ def test_index_kl_128k_sampled_rows():
         res = orc.prefill(host["q"], host["k"], host["v"], host["q_idx"], host["k_idx"], k,
                           rows=rows)
         gidx = idx[lo:lo + 16].cpu().numpy()
-        differ = parity.check_selection(gidx, res["sel"], res["near_tie"], k, label=f"rows {lo}")
+        differ = parity.check_selection(gidx, res, k, rows // orc.BLOCK, label=f"rows {lo}")
         ref = orc.index_kl(host["q"], host["k"], host["q_idx"], host["k_idx"],
                            orc.selection_array(res["sel"], k), scale, q_begin=lo)
         keep = np.array([not any((i, g) in differ for g in range(G)) for i in range(16)])

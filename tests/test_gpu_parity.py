@@ -59,6 +59,9 @@ PREFILL_CASES = [
     (1200, 2, 3, 128, 8, "bf16", 2),    # 3 heads: rows 30, 31 of every row tile unused
     (3500, 2, 2, 128, 24, "bf16", 3),   # top_k 24 > 16: the two-step index branch, wide lists
     (700, 64, 1, 64, 3, "bf16", 1),     # the most groups the ABI allows
+    (1300, 2, 4, 128, 1, "bf16", 2),    # top_k 1: only the forced local block
+    (900, 2, 3, 64, 1, "f32", 0),       # top_k 1, fp32
+    (1100, 2, 3, 128, 4, "f32", 0),     # fp32 with index dim 128
 ]
 
 
@@ -183,7 +186,7 @@ def test_index_topk_fused(T, G, Hpg, d_idx, top_k, dtype, planted):
     fused = msa.alloc_block_idx(p)
     msa.msa_index_topk(p, xd["q_idx"], xd["k_idx"], fused)
     torch.cuda.synchronize()
-    parity.check_selection(fused.cpu().numpy(), res["sel"], res["near_tie"], top_k, label="fused")
+    parity.check_selection(fused.cpu().numpy(), res, top_k, rows // orc.BLOCK, label="fused")
 
 
 def test_prefill_pipeline_fused_index():
@@ -213,6 +216,10 @@ DECODE_CASES = [
     (2, 5000, [5000, 3333], 4, 8, 128, 40, "bf16", 4),  # top_k 40; 27 blocks < k: all kept
     (1, 9000, [9000], 2, 4, 128, 64, "bf16", 3),         # the largest top_k: 64 of 71 blocks
     (2, 2000, [2000, 1500], 20, 2, 128, 4, "bf16", 2),   # G > 16: the general scan kernel
+    (3, 3000, [3000, 1, 1537], 4, 8, 64, 4, "bf16", 2),  # bf16 with index dim 64
+    (2, 2500, [2500, 1000], 2, 3, 128, 4, "f32", 0),     # fp32 with index dim 128
+    (3, 2000, [2000, 129, 1], 4, 8, 128, 1, "bf16", 0),  # top_k 1: only the local block
+    (2, 1500, [1500, 700], 2, 3, 64, 1, "f32", 0),       # top_k 1, fp32
 ]
 
 
@@ -244,6 +251,7 @@ def test_decode_equals_last_prefill_row():
     (3, 4096, 8, 8, 128, 16, "bf16", [4096, 1000, 129]),   # LDS scan, ragged lengths
     (2, 2048, 20, 2, 64, 5, "f32", [2048, 777]),           # generic scan (G > 16, d = 64)
     (2, 1024, 4, 4, 128, 3, "bf16", [1, 300]),              # L = 1, all blocks kept
+    (2, 1024, 4, 4, 128, 1, "bf16", [1024, 500]),           # top_k 1: the local block only
 ])
 def test_paged_decode_equals_contiguous(B, L, G, Hpg, d_idx, top_k, dtype, lens):
     """The paged decode entries on pages scattered at random ids give bit-identical block

@@ -230,3 +230,96 @@ def test_attend_is_order_free_and_softmax_sums():
     o = orc.attend(q1, k2, v2, 0.5)
     p = 1.0 / (1.0 + math.exp(-1.0))
     assert abs(o[0, 0] - p) < 1e-15 and abs(o[0, 1] - (1 - p)) < 1e-15
+
+
+# -- Helpers the device comparison relies on ------------------------------------------
+
+def test_as_f64_widens_bf16_exactly():
+    """Catches: a bf16 pattern widened from the wrong half, sign or exponent lost, or
+    subnormals flushed. Hand-computed values of bf16 bit patterns (sign, 8-bit exponent
+    with bias 127, 7 stored fraction bits), and torch's own bf16 -> float64 conversion."""
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0 + 2.0 ** -7, 0x4049: 3.140625,
+             0x0001: 2.0 ** -133, 0x8000: -0.0, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+             0x3E80: 0.25, 0xBF40: -0.75}
+    bits = np.array(list(cases.keys()), dtype=np.uint16)
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    got = orc.as_f64(t)
+    want = np.array(list(cases.values()), dtype=np.float64)
+    assert got.dtype == np.float64
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    rnd = torch.randn(4096, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    assert np.array_equal(orc.as_f64(rnd), rnd.to(torch.float64).numpy())
+    assert np.array_equal(orc.as_f64(rnd[100:200]), rnd[100:200].to(torch.float64).numpy())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attend_on_selection_equals_masked_sdpa(dtype):
+    """Catches: padding ids not skipped, blocks beyond the query's position attended, the
+    causal cut inside the local block, a wrong scale. attend_on_selection over an arbitrary
+    valid selection (not the oracle's own) equals torch's fp64 attention with the mask of
+    that selection; over every visible block it equals dense causal attention."""
+    T, G, Hpg, D = 700, 2, 3, 32
+    x = synth.prefill_inputs(T, G, Hpg, D, 16, dtype=dtype, seed=12)
+    rng = np.random.default_rng(4)
+    dense = _sdpa(x["q"], x["k"], x["v"], causal=True)
+    for t in (0, 127, 128, 300, 555, 699):
+        b = t // 128
+        others = rng.choice(b, size=min(b, 2), replace=False) if b else np.zeros(0, int)
+        sel = np.concatenate([np.sort(others), [b], [-1, -1]]).astype(np.int32)
+        for g in range(G):
+            hs = slice(g * Hpg, (g + 1) * Hpg)
+            got = orc.attend_on_selection(x["q"][t, hs], x["k"][g], x["v"][g], sel, t)
+            mask = np.zeros((Hpg, 1, T), dtype=bool)
+            for c in sel[sel >= 0]:
+                mask[:, :, c * 128: min(c * 128 + 128, t + 1)] = True
+            qq = torch.as_tensor(orc.as_f64(x["q"][t, hs]))[:, None, :]
+            kk = torch.as_tensor(orc.as_f64(x["k"][g]))[None].expand(Hpg, T, D)
+            vv = torch.as_tensor(orc.as_f64(x["v"][g]))[None].expand(Hpg, T, D)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, kk, vv, attn_mask=torch.as_tensor(mask))[:, 0].numpy()
+            assert np.max(np.abs(got - ref)) < 1e-12, (t, g)
+            full = orc.attend_on_selection(x["q"][t, hs], x["k"][g], x["v"][g],
+                                           np.arange(b + 1), t)
+            assert np.max(np.abs(full - dense[t, hs])) < 1e-12, (t, g)
+    with pytest.raises(AssertionError):  # a repeated id would weigh a block twice
+        orc.attend_on_selection(x["q"][500, :Hpg], x["k"][0], x["v"][0], [1, 1, 3], 500)
+
+
+def _tie_case():
+    """Oracle result for one crafted row: local block 6, top_k 4, the 3rd and 4th best
+    earlier scores 1e-7 apart relative (a declared near tie)."""
+    scores = np.array([5.0, 1.0, 3.0, 3.0000001, 0.5, 4.0])
+    b, top_k = 6, 4
+    sel, tie = orc.select_blocks(scores, b, top_k)
+    assert tie and sel.tolist() == [0, 3, 5, 6]
+    res = dict(sel=[[sel]], near_tie=np.array([[tie]]), block_scores={(0, 0): scores})
+    return res, b, top_k
+
+
+def test_check_selection_validates_near_tie_rows():
+    """Catches a comparison that waves any device set through on a near-tie row: the
+    allowed swap (block 2 for block 3, scores within the gap) passes; a dropped local
+    block, a repeated id, a low-scoring block, a short list, ids out of order and a
+    differing row without a near tie all fail."""
+    from tests import parity
+    res, b, top_k = _tie_case()
+    ok = np.array([[[0, 2, 5, 6]]], dtype=np.int32)
+    assert parity.check_selection(ok, res, top_k, [b]) == {(0, 0)}
+    assert parity.check_selection(np.array([[[0, 3, 5, 6]]], dtype=np.int32), res, top_k,
+                                  [b]) == set()
+    bad = {
+        "local dropped": [0, 2, 3, 5],
+        "repeated id": [0, 2, 2, 6],
+        "low score": [0, 1, 5, 6],
+        "short": [0, 5, 6, -1],
+        "out of order": [2, 0, 5, 6],
+        "future block": [0, 2, 6, 7],
+    }
+    for name, row in bad.items():
+        with pytest.raises(AssertionError):
+            parity.check_selection(np.array([[row]], dtype=np.int32), res, top_k, [b])
+            pytest.fail(name)
+    res["near_tie"][0, 0] = False
+    with pytest.raises(AssertionError):
+        parity.check_selection(ok, res, top_k, [b])
