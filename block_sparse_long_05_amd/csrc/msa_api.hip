@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "msa_launch.h"
 
 using namespace msa;
@@ -95,6 +98,35 @@ size_t kl_ws_bytes(const msa_problem* p) {
 
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// Scratch of the allocation-free decode entry point. Each GPU that runs the library holds
+// its own copy from the module's load until the process ends. In host code `scratch`
+// names only a host-side stand-in: its device address comes from hipGetSymbolAddress, once
+// per device, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (looked up on the device's first call).
+msa_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MSA_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return MSA_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MSA_OK;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q, const void* k,
@@ -156,7 +188,10 @@ const char* msa_status_string(msa_status s) {
     case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT: bad pointer, range or enum";
     case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: dimension or option not built";
     case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL: see msa_workspace_size";
-    case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch failed";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch or runtime query failed";
+    case MSA_ERR_TOO_LARGE:
+      return "MSA_ERR_TOO_LARGE: the problem exceeds the fixed scratch of an allocation-free "
+             "entry point";
   }
   return "MSA_ERR_UNKNOWN";
 }
@@ -325,6 +360,23 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
     return MSA_ERR_INVALID_ARGUMENT;
   return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
                               workspace_bytes, as_stream(stream));
+}
+
+msa_status msa_sparse_attn_decode_noalloc(const msa_problem* p, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const int32_t* block_idx, void* out, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_idx) ||
+      !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (decode_ws_bytes(p, false) > MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != MSA_OK) return st;
+  return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, ws,
+                              MSA_NOALLOC_SCRATCH_BYTES, as_stream(stream));
 }
 
 namespace {

@@ -22,6 +22,8 @@ MSA_ERR_INVALID_ARGUMENT = 1
 MSA_ERR_UNSUPPORTED = 2
 MSA_ERR_WORKSPACE_TOO_SMALL = 3
 MSA_ERR_HIP = 4
+MSA_ERR_TOO_LARGE = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MSA_NOALLOC_SCRATCH_BYTES
 
 DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"prefill": 0, "decode": 1}
@@ -33,7 +35,8 @@ BLOCK = 128
 
 # Every symbol include/msa.h declares.
 EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
-            "msa_sparse_attn_decode", "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
+            "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc",
+            "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
             "msa_index_kl_prefill", "msa_dense_gqa_attn", "msa_workspace_size",
             "msa_status_string", "msa_abi_version"]
 
@@ -74,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_topk.argtypes = [pp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_decode_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp]
     lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.msa_index_scores_paged.argtypes = [pp, vp, vp, vp, i32, i64, vp, vp]
@@ -86,7 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_abi_version.argtypes = []
     for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
                  "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
-                 "msa_sparse_attn_decode", "msa_dense_gqa_attn", "msa_workspace_size",
+                 "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc",
+                 "msa_dense_gqa_attn", "msa_workspace_size",
                  "msa_index_kl_prefill",
                  "msa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -225,6 +230,15 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, block_idx, out, work
     _check(load_library().msa_sparse_attn_decode(
         ctypes.byref(p.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_idx), _ptr(out),
         _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode")
+
+
+def msa_sparse_attn_decode_noalloc(p: Problem, q, k_cache, v_cache, block_idx, out,
+                                   stream=None):
+    """msa_sparse_attn_decode without a workspace: the library's fixed per-GPU scratch holds
+    the split partials (see include/msa.h). The stream must belong to the current device."""
+    _check(load_library().msa_sparse_attn_decode_noalloc(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_idx), _ptr(out),
+        _stream(stream)), "msa_sparse_attn_decode_noalloc")
 
 
 def msa_index_kl_prefill(p: Problem, q, k, q_idx, k_idx, block_idx, index_scale: float, loss,

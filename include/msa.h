@@ -15,7 +15,9 @@
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
  *     row-major and 16-byte aligned. The library never allocates, frees, copies to
  *     the host or synchronises; work is enqueued in order on `stream` (a
- *     hipStream_t; NULL = the default stream). Calls are stateless and re-entrant.
+ *     hipStream_t; NULL = the default stream). Calls are stateless and re-entrant,
+ *     except msa_sparse_attn_decode_noalloc, whose fixed per-GPU scratch is shared by
+ *     all of its calls on that GPU (see there).
  *   - All argument checks run on the host before any launch, so every error return
  *     below happens without touching the device. A failed launch returns
  *     MSA_ERR_HIP; faults inside kernels surface at the caller's next sync.
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 #define MSA_BLOCK_SIZE 128
 #define MSA_HEAD_DIM 128
 #define MSA_MAX_TOPK 64
@@ -55,7 +57,9 @@ typedef enum {
   MSA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad range, bad enum */
   MSA_ERR_UNSUPPORTED = 2,         /* valid but not built: head_dim, index_dim, block size, ... */
   MSA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < msa_workspace_size(...) */
-  MSA_ERR_HIP = 4                  /* a kernel launch failed */
+  MSA_ERR_HIP = 4,                 /* a kernel launch (or a runtime query) failed */
+  MSA_ERR_TOO_LARGE = 5            /* needs more than the fixed scratch of an allocation-free
+                                      entry point (MSA_NOALLOC_SCRATCH_BYTES) */
 } msa_status;
 
 typedef enum { MSA_DTYPE_F32 = 0, MSA_DTYPE_BF16 = 1 } msa_dtype;
@@ -164,6 +168,29 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
 msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_idx, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of msa_sparse_attn_decode, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results (bit for bit) as msa_sparse_attn_decode,
+ * minus the workspace: the split partials live in a fixed scratch array of
+ * MSA_NOALLOC_SCRATCH_BYTES that the library holds once per GPU, from that GPU's first call
+ * until the process ends. Neither this call nor its kernels allocate or free anything.
+ *   - A problem whose msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_DECODE) exceeds
+ *     MSA_NOALLOC_SCRATCH_BYTES returns MSA_ERR_TOO_LARGE before anything else runs
+ *     (32 MiB holds bf16 problems with B * G * Hpg * top_k <= 64512, e.g. 63 sequences of
+ *     8 groups x 8 heads x 16 blocks; fp32 splits each block in two and holds half that).
+ *   - `stream` must belong to the calling thread's current device (hipSetDevice): the
+ *     scratch used is that device's copy.
+ *   - Every call on one GPU shares that GPU's scratch, and each call overwrites what the
+ *     previous one left there (nothing in it needs to start at zero). Calls whose work
+ *     overlaps on one GPU (the same stream is fine; different streams, or different host
+ *     threads, without ordering between them, are not) race and give unspecified results.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+msa_status msa_sparse_attn_decode_noalloc(const msa_problem* p, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const int32_t* block_idx, void* out, void* stream);
 
 /*
  * Paged decode (the GQA KV cache as a server keeps it, reused as is: researchpapers.dev

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msa.load_library()
-    assert lib.msa_abi_version() == 2
+    assert lib.msa_abi_version() == 3
     for s in range(5):
         assert msa.status_string(s).startswith("MSA_")
 
@@ -301,3 +301,31 @@ def test_python_helpers_reject_mismatched_inputs():
               dec(q=torch.zeros(B, 5, 128, dtype=torch.bfloat16))]:
         with pytest.raises(ValueError):
             msa.decode(x, 4)
+
+
+def test_noalloc_decode_validation():
+    """The allocation-free decode entry refuses, on the host, what does not fit its fixed
+    scratch (MSA_ERR_TOO_LARGE) and what the regular entry refuses; nothing reaches the
+    device."""
+    lib = msa.load_library()
+    call = lib.msa_sparse_attn_decode_noalloc
+    assert msa.NOALLOC_SCRATCH_BYTES == 32 << 20
+    # bf16, G = Hpg = 8, top_k = 16: 1024 head-blocks per sequence, 520 bytes each
+    n = ctypes.c_size_t(0)
+    for B, fits in ((63, True), (64, False), (65535, False)):
+        c = _decode(batch=B)
+        assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
+                                      ctypes.byref(n)) == msa.MSA_OK
+        assert (n.value <= msa.NOALLOC_SCRATCH_BYTES) == fits
+        if not fits:
+            assert call(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_TOO_LARGE
+    c32 = _decode(batch=32, dtype="f32")   # fp32 splits blocks in two: 65536 head-halves
+    assert call(ctypes.byref(c32), FAKE, FAKE, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_TOO_LARGE
+    c = _decode(batch=4)
+    assert call(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE + 4, 0) == \
+        msa.MSA_ERR_INVALID_ARGUMENT                                  # misaligned out
+    assert call(ctypes.byref(c), 0, FAKE, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(ctypes.byref(_prefill().c()), FAKE, FAKE, FAKE, FAKE, FAKE, 0) == \
+        msa.MSA_ERR_INVALID_ARGUMENT                                  # prefill problem
+    assert call(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert "scratch" in msa.status_string(msa.MSA_ERR_TOO_LARGE)
