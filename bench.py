@@ -11,6 +11,9 @@ Each is timed with HIP events on the stream the kernels run on, after W untimed
 warmup steps; the dominant kernel of each is also timed launch by launch for its
 roofline fraction. The CPU oracle is then timed on a bounded sample of the same
 inputs (and the sampled rows are checked against the GPU result).
+Then the other workloads of the same metric run as extra legs with their own settings
+(EXTRA_LEGS): the 1,048,576-token prefill with its dense GQA baseline, the 4096-token fp32
+prefill (every row checked against the oracle) and the 4 x 131072 decode step.
 
 One JSON line goes to stdout; progress goes to stderr.
 """
@@ -44,6 +47,16 @@ WORKLOADS = {
                       dtype="bf16"),
     "decode_128k": dict(kind="decode", B=4, L=131072, G=8, Hpg=8, d_idx=128, top_k=16,
                         planted=16, dtype="bf16"),
+}
+
+# Settings of the legs that run after the two headline legs (the other workloads of the
+# same metric). The 1M prefill keeps its step count small (about a second a step) and runs
+# its dense baseline once; the small workloads check every row against the oracle.
+EXTRA_LEGS = {
+    "prefill_1m": dict(steps=2, warmup=1, kl=0, gemm_calibration=0, dense_reps=1,
+                       dense_warm=False, cpu_seconds=10.0, paged=0),
+    "prefill_4k_f32": dict(kl=0, gemm_calibration=0, dense_reps=5, oracle_all_rows=True),
+    "decode_128k": dict(dense_reps=5),
 }
 
 
@@ -98,9 +111,11 @@ def dense_decode_bytes(lens, G, Hpg, D, esize):
     return sum(2 * G * L * D * esize + 2 * G * Hpg * D * esize for L in lens)
 
 
-def time_reps(torch, fn, reps):
-    """Mean milliseconds of fn() over reps runs after one untimed run (HIP events)."""
-    fn()
+def time_reps(torch, fn, reps, warm=True):
+    """Mean milliseconds of fn() over reps runs, after one untimed run when warm (HIP
+    events)."""
+    if warm:
+        fn()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,7 +353,8 @@ def run_prefill(name, cfg, args, torch, msa, synth):
         def dense_step():
             for p in probs:
                 msa.msa_dense_gqa_attn(p, q, x["k"], x["v"], dout)
-        dense_ms = time_reps(torch, dense_step, args.dense_reps)
+        dense_ms = time_reps(torch, dense_step, args.dense_reps,
+                             warm=getattr(args, "dense_warm", True))
         del dout
         dense_flops = dense_prefill_flops(T, G * Hpg, 128)
         res["dense"] = dict(ms=dense_ms, tflops=dense_flops / (dense_ms * 1e-3) / 1e12,
@@ -364,11 +380,15 @@ def prefill_oracle_sample(name, cfg, x, out, idx_full, args):
     T, top_k = cfg["T"], cfg["top_k"]
     host = {k: x[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
     nblk = (T + BLOCK - 1) // BLOCK
-    order = np.linspace(nblk - 1, 0, num=min(nblk, 64)).astype(int)
+    all_rows = getattr(args, "oracle_all_rows", False)
+    if all_rows:   # every row, one query block at a time, latest first
+        slices = [np.arange(b * BLOCK, min(b * BLOCK + BLOCK, T)) for b in range(nblk - 1, -1, -1)]
+    else:          # 32-token slices of evenly spaced query blocks, latest first
+        order = np.linspace(nblk - 1, 0, num=min(nblk, 64)).astype(int)
+        slices = [np.arange(int(b) * BLOCK + (j % 4) * 32, min(int(b) * BLOCK + (j % 4) * 32 + 32, T))
+                  for j, b in enumerate(order)]
     done, secs, worst, ties, differ, nsl = 0, 0.0, 0.0, 0, 0, 0
-    for j, b in enumerate(order):
-        lo = int(b) * BLOCK + (j % 4) * 32
-        rows = np.arange(lo, min(lo + 32, T))
+    for rows in slices:
         if len(rows) == 0:
             continue
         t0 = time.perf_counter()
@@ -384,14 +404,16 @@ def prefill_oracle_sample(name, cfg, x, out, idx_full, args):
         worst = max(worst, info["err"])
         ties += info["near_ties"]
         differ += info["differ"]
-        if secs >= args.cpu_seconds:
+        if secs >= args.cpu_seconds and not all_rows:
             break
     cores = blas_threads()
-    base = dict(value=done / secs, unit="tok/s", cores=cores, kind="oracle",
-                sample=f"{done} query tokens x {cfg['G']} groups in {nsl} slices of 32 tokens "
-                       f"from evenly spaced query blocks of the same {T}-token input, latest "
-                       f"first (whole rows: index scores over all earlier keys, top-k, "
-                       f"attention)",
+    sample = (f"all {T} query tokens x {cfg['G']} groups of the input (whole rows: index scores "
+              f"over all earlier keys, top-k, attention)" if all_rows else
+              f"{done} query tokens x {cfg['G']} groups in {nsl} slices of 32 tokens "
+              f"from evenly spaced query blocks of the same {T}-token input, latest "
+              f"first (whole rows: index scores over all earlier keys, top-k, "
+              f"attention)")
+    base = dict(value=done / secs, unit="tok/s", cores=cores, kind="oracle", sample=sample,
                 seconds=secs, cpu=cpu_model())
     par = dict(rows_checked=done, max_abs_err=worst, near_tie_rows=ties,
                near_tie_selection_differences=differ, ok=True)
@@ -560,7 +582,9 @@ def run_decode(name, cfg, args, torch, msa, synth):
         dense_bytes = dense_decode_bytes(lens, G, Hpg, 128, esize)
         res["dense"] = dict(us_per_step=dense_ms * 1e3, gbs=dense_bytes / (dense_ms * 1e-3) / 1e9,
                             frac_of_hbm=dense_bytes / (dense_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                            speedup=dense_ms / ms_plain)
+                            speedup=dense_ms / ms_plain,
+                            kernel="decode_dense_bf16" if cfg["dtype"] == "bf16"
+                            else "gather_attn (dense decode)")
         del dws, dout
     log(f"[{name}] {res['us_per_step']:.1f} us/step {res['us_per_token']:.2f} us/token  "
         f"kernels {res['kernel_us']}  path {res['path_gbs']:.0f} GB/s "
@@ -643,6 +667,9 @@ def main():
     ap.add_argument("--gemm-calibration", type=int, default=1,
                     help="also time the vendor bf16 GEMM (16384^3, N(0,1) operands) and report "
                          "the prefill path against it (1/0)")
+    ap.add_argument("--extra", default=",".join(EXTRA_LEGS),
+                    help="comma-separated workloads run after the two headline legs, each with "
+                         "its own settings (EXTRA_LEGS); 'none' to skip")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -670,6 +697,16 @@ def main():
     if args.decode != "none":
         dec = run_decode(args.decode, WORKLOADS[args.decode], args, torch, msa, synth)
 
+    extra = {}
+    for name in ([] if args.extra in ("", "none") else args.extra.split(",")):
+        if name in (args.prefill, args.decode):
+            continue
+        leg = argparse.Namespace(**vars(args))
+        for k, v in EXTRA_LEGS.get(name, {}).items():
+            setattr(leg, k, v)
+        runner = run_prefill if WORKLOADS[name]["kind"] == "prefill" else run_decode
+        extra[name] = runner(name, WORKLOADS[name], leg, torch, msa, synth)
+
     if pre is None and dec is None:
         return
     head = pre if pre is not None else dec
@@ -689,13 +726,36 @@ def main():
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": hib, "scaling": "weak",
         "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic: seeded N(0,1) inputs with planted index blocks",
-        "config": config, "roofline": head["roofline"],
+        "config": config, "roofline": dict(head["roofline"]),
         "cpu_baseline": head.get("cpu_baseline"),
     }
+    # The roofline object is the dominant kernel's (its algorithmic work per launch over its
+    # launch time); the whole step against the same peak sits beside it as `path`, with the
+    # target fraction for the step.
+    if pre is not None:
+        line["roofline"]["path"] = dict(
+            achieved=pre["path_tflops"], peak=line["roofline"]["peak"], unit="TFLOP/s",
+            frac=pre["path_frac_of_peak"], target_frac=0.5,
+            target_met=pre["path_frac_of_peak"] >= 0.5,
+            what="index + attention FLOPs of the whole prefill step / step time")
+        line["path_frac_of_peak"] = pre["path_frac_of_peak"]
+    else:
+        line["roofline"]["path"] = dict(
+            achieved=dec["path_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+            frac=dec["path_frac_of_hbm"], target_frac=0.6,
+            target_met=dec["path_frac_of_hbm"] >= 0.6,
+            what="algorithmic bytes of the whole decode step / step time")
     if pre is not None:
         line["prefill"] = pre
     if dec is not None:
+        dec["roofline"] = dict(dec["roofline"], path=dict(
+            achieved=dec["path_gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+            frac=dec["path_frac_of_hbm"], target_frac=0.6,
+            target_met=dec["path_frac_of_hbm"] >= 0.6,
+            what="algorithmic bytes of the whole decode step / step time"))
         line["decode"] = dec
+    if extra:
+        line["extra"] = extra
     print(json.dumps(line), flush=True)
 
 

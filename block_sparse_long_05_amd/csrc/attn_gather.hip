@@ -347,12 +347,24 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     }
     L += wave_sum_xor(w * l, 1);
     const int cnt = min(64, nsplit - s0);
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-      const float2 o = *reinterpret_cast<const float2*>(
-          part_o + ((bg * nsplit + s0 + k) * Hpg + h) * kHeadDim + 2 * lane);
-      a0 += wk * o.x;
-      a1 += wk * o.y;
+    // 32 partials requested at a time (one wait per 32, not one per partial)
+    for (int k0 = 0; k0 < cnt; k0 += kFew) {
+      float2 o[kFew];
+#pragma unroll
+      for (int k = 0; k < kFew; ++k)
+        o[k] = k0 + k < cnt ? *reinterpret_cast<const float2*>(
+                                  part_o + ((bg * nsplit + s0 + k0 + k) * Hpg + h) * kHeadDim +
+                                  2 * lane)
+                            : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < kFew; ++k) {
+        if (k0 + k < cnt) {
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k0 + k));
+          a0 += wk * o[k].x;
+          a1 += wk * o[k].y;
+        }
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -60,10 +60,21 @@ bool decode_block_kernel(const msa_problem* p, bool dense) {
   return !dense && p->dtype == MSA_DTYPE_BF16;
 }
 
+// Dense bf16 decode streams each (sequence, group) cache in a few long splits.
+bool decode_dense_stream_kernel(const msa_problem* p, bool dense) {
+  return dense && p->dtype == MSA_DTYPE_BF16;
+}
+
 void decode_split(const msa_problem* p, bool dense, int* nsplit, int* bps) {
   if (!dense) {
     *nsplit = decode_block_kernel(p, dense) ? p->top_k : 2 * p->top_k;
     *bps = 1;
+    return;
+  }
+  if (decode_dense_stream_kernel(p, dense)) {
+    int64_t kps;
+    dense_decode_plan(p->batch, p->num_groups, p->max_len, nsplit, &kps);
+    *bps = 0;
     return;
   }
   const int64_t nblk = nblk_of(p);
@@ -143,6 +154,14 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             align_up(units * MSA_HEAD_DIM * sizeof(float)));
   const int bf16 = p->dtype == MSA_DTYPE_BF16;
+  if (decode_dense_stream_kernel(p, dense)) {
+    hipError_t e = launch_decode_dense_bf16(q, k, v, p->seq_lens, p->batch, p->max_len,
+                                            p->num_groups, p->heads_per_group, part_o, part_ml,
+                                            st);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(launch_decode_combine(bf16, part_o, part_ml, out, p->batch,
+                                            p->num_groups, p->heads_per_group, nsplit, st));
+  }
   if (decode_block_kernel(p, dense)) {
     hipError_t e = launch_decode_attn_bf16(q, k, v, block_idx, p->seq_lens, p->batch,
                                            p->max_len, p->num_groups, p->heads_per_group,

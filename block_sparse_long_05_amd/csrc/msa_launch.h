@@ -81,6 +81,13 @@ hipError_t launch_decode_attn_bf16(const void* q, const void* k, const void* v,
                                    int64_t max_len, int G, int Hpg, int top_k, PageMap pm,
                                    float* part_o, float* part_ml, hipStream_t st);
 
+// Dense decode attention, bf16 (decode_attn.hip): one partial per (sequence, group, split of
+// keys_per_split cache keys), nsplit splits per (sequence, group), as dense_decode_plan sets.
+void dense_decode_plan(int B, int G, int64_t max_len, int* nsplit, int64_t* keys_per_split);
+hipError_t launch_decode_dense_bf16(const void* q, const void* k, const void* v,
+                                    const int32_t* seq_lens, int B, int64_t max_len, int G,
+                                    int Hpg, float* part_o, float* part_ml, hipStream_t st);
+
 // Fixed-order log-sum-exp merge of decode partials into out [B, Hq, 128].
 hipError_t launch_decode_combine(int bf16, const float* part_o, const float* part_ml, void* out,
                                  int B, int G, int Hpg, int nsplit, hipStream_t stream);
