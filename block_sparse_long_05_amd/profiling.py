@@ -59,8 +59,11 @@ def source_hash(kernel_name: str):
 
 
 def short_name(name: str) -> str:
-    base = name.split("(")[0].replace("void ", "")
-    return base.strip()
+    base = name.split("(")[0].replace("void ", "").strip()
+    if base.startswith("Cijk_"):  # a hipBLASLt GEMM kernel: its tile and MFMA shape suffice
+        parts = [x for x in base.split("_") if x.startswith(("MT", "MI"))]
+        return "hipBLASLt GEMM " + " ".join(parts[:2])
+    return base
 
 
 def stats_text(stats_csv: str, cmd: str = "") -> str:
@@ -149,6 +152,68 @@ def traffic_text(t: dict, workloads: str = "") -> str:
     return "\n".join(out) + "\n"
 
 
+def _agent(directory: str) -> dict:
+    for f in glob.glob(os.path.join(directory, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Name", "").startswith("gfx"):
+                return r
+    return {}
+
+
+def mfma_text(directory: str, cmd: str = "", min_ms: float = 0.1) -> str:
+    """MFMA use per kernel from a --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 run: the shader clock the kernel ran at (GRBM_GUI_ACTIVE per
+    XCD over the dispatch time), the fraction of SIMD cycles the matrix cores were busy
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x SIMDs): the profiler's MfmaUtil),
+    and the bf16 MFMA FLOP/s the MOPS counter implies (512 FLOP per unit) against the spec
+    peak and against the peak at the measured clock (CUs x 4096 bf16 FLOP per cycle)."""
+    agent = _agent(directory)
+    nxcc = int(agent.get("Num_Xcc", 8))
+    simds = int(agent.get("Simd_Count", 1024))
+    cus = int(agent.get("Cu_Count", 256))
+    fmax = float(agent.get("Max_Engine_Clk_Fcompute", 2400)) * 1e6
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = short_name(r.get("Kernel_Name") or "")
+            acc[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                acc[name]["_ns"].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    out = ["MFMA use per kernel from rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES "
+           "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 (one run)",
+           f"device: {agent.get('Name', '?')}, {cus} CUs, {simds} SIMDs, {nxcc} XCDs, "
+           f"max shader clock {fmax / 1e9:.2f} GHz; bf16 peak {cus * 4096 * fmax / 1e12:.0f} "
+           f"TFLOP/s at that clock"]
+    if cmd:
+        out.append(f"command: {cmd}")
+    out += ["clock = GRBM_GUI_ACTIVE / XCDs / dispatch time; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES "
+            "/ (GRBM_GUI_ACTIVE / XCDs x SIMDs); TF/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / "
+            "dispatch time; frac_at_clock = TF/s over CUs x 4096 x clock",
+            "",
+            f"{'calls':>5} {'avg_ms':>9} {'clock_GHz':>9} {'mfma_busy':>9} {'TF/s':>7} "
+            f"{'frac_spec':>9} {'frac_at_clock':>13} {'bf16_FLOP':>10}  kernel"]
+    rows = []
+    for name, c in acc.items():
+        if not c.get("_ns") or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        ns = sum(c["_ns"]) / len(c["_ns"])
+        if ns < min_ms * 1e6:
+            continue
+        g = sum(c["GRBM_GUI_ACTIVE"]) / len(c["GRBM_GUI_ACTIVE"]) / nxcc
+        clk = g / (ns * 1e-9)
+        busy = (sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])) /
+                max(1, len(c.get("SQ_VALU_MFMA_BUSY_CYCLES", [0])))) / (g * simds)
+        mops = sum(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])) / max(
+            1, len(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])))
+        tf = 512.0 * mops / (ns * 1e-9) / 1e12
+        rows.append((ns, len(c["_ns"]), clk, busy, tf, 512.0 * mops, name))
+    for ns, n, clk, busy, tf, fl, name in sorted(rows, reverse=True):
+        out.append(f"{n:5d} {ns / 1e6:9.3f} {clk / 1e9:9.2f} {busy:9.3f} {tf:7.0f} "
+                   f"{tf * 1e12 / (cus * 4096 * fmax):9.3f} "
+                   f"{(tf * 1e12 / (cus * 4096 * clk)) if clk > 0 else 0:13.3f} {fl:10.3e}  {name}")
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -163,12 +228,18 @@ def main():
     b.add_argument("--cmd", default="")
     b.add_argument("--bench-log", default="",
                    help="output of the profiled bench.py run (its workloads and launches)")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--cmd", default="")
+    m.add_argument("--min-ms", type=float, default=0.1)
     c = sub.add_parser("traffic-text")
     c.add_argument("json")
     c.add_argument("--workloads", default="")
     args = ap.parse_args()
     if args.what == "stats":
         print(stats_text(args.csv, args.cmd), end="")
+    elif args.what == "mfma":
+        print(mfma_text(args.dir, args.cmd, args.min_ms), end="")
     elif args.what == "traffic-text":
         print(traffic_text(json.load(open(args.json)), args.workloads), end="")
     else:
