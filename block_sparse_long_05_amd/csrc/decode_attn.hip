@@ -32,7 +32,7 @@ __device__ __forceinline__ void rows32_dma(const uint16_t* blk, int row0, int nv
     const int rr = min(row0 + r, nvalid - 1);
     __builtin_amdgcn_global_load_lds((const void*)(blk + rr * kHeadDim + chunk * 8),
                                      (__attribute__((address_space(3))) void*)(buf + i * 1024),
-                                     16, 0, 0);
+                                     16, 0, kLoadOnce);
   }
 }
 
@@ -186,7 +186,7 @@ __device__ __forceinline__ void rows32_dma_seq(const uint16_t* base, int64_t row
     const int64_t rr = min(row0 + r, len - 1);
     __builtin_amdgcn_global_load_lds((const void*)(base + rr * kHeadDim + chunk * 8),
                                      (__attribute__((address_space(3))) void*)(buf + i * 1024),
-                                     16, 0, 0);
+                                     16, 0, kLoadOnce);
   }
 }
 

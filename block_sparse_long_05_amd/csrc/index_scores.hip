@@ -513,7 +513,8 @@ __device__ __forceinline__ void scan_issue_stage(const uint16_t* rows, uint8_t* 
     const int chunk = p ^ (r & 15);
     const uint16_t* src = rows + (int64_t)r * 128 + chunk * 8;
     __builtin_amdgcn_global_load_lds(
-        (const void*)src, (__attribute__((address_space(3))) void*)(stage_lds + i * 1024), 16, 0, 0);
+        (const void*)src, (__attribute__((address_space(3))) void*)(stage_lds + i * 1024), 16, 0,
+        kLoadOnce);
   }
 }
 

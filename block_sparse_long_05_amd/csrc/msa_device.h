@@ -16,6 +16,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Cache policy of direct global->LDS loads of data that is read once (a decode step streams
+// the whole index-key cache and each kept K/V block once): non-temporal (gfx950 "nt"), so the
+// stream does not evict reusable lines. Measured on the 8 x 1M decode scan: 311 us instead of
+// 361 us for the same 2.15 GB.
+constexpr int kLoadOnce = 2;
+
 constexpr int kBlock = 128;
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
