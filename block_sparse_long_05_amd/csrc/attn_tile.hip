@@ -38,6 +38,8 @@
 namespace msa {
 
 constexpr int kTile = 256;                 // sorted entries per workgroup
+constexpr int kTileF32 = 64;               // the same for the fp32 tile kernel
+constexpr int kQtileWavesF32 = 4;          // row tiles (waves) of an fp32 query tile
 constexpr int kKRow = kHeadDim + 8;        // LDS row stride of K (elements)
 constexpr int kVRow = kBlock + 4;          // LDS row stride of V^T (elements)
 
@@ -53,10 +55,10 @@ __global__ void kv_zero_kernel(int32_t* __restrict__ p, int64_t n) {
 __device__ __forceinline__ int frag_pos(int dt, int jj, int q) { return 64 * q + 16 * dt + 4 * jj; }
 
 // Query tiles: the rows of one 32-row MFMA tile are floor(32 / Hpg) tokens x Hpg heads,
-// and a query tile is the 8 row tiles of one workgroup.
+// and a query tile is the row tiles of one workgroup: 8 for bf16, 4 for fp32 (whose
+// problems are small: more workgroups fill the chip).
 __host__ __device__ __forceinline__ int qtile_tokens(int Hpg, int bf16) {
-  (void)bf16;
-  return 8 * (32 / Hpg);
+  return (bf16 ? 8 : kQtileWavesF32) * (32 / Hpg);
 }
 
 // True when block c is in the tile's shared list (ascending, -1 padded).
@@ -473,7 +475,9 @@ struct KvStage {
   }
 };
 
-template <class E>
+// TILE sorted entries per workgroup (the fp32 path takes small tiles: its problems are small,
+// and more workgroups fill the chip).
+template <class E, int TILE = kTile>
 __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const int32_t* __restrict__ block_idx,
@@ -485,17 +489,17 @@ __global__ __launch_bounds__(256, 1) void kv_attn_kernel(
   constexpr int kBufs = E::is_bf16 ? 2 : 1;
   __shared__ __align__(16) elem Ks[kBufs][kBlock * kKRow];
   __shared__ __align__(16) elem Vt[kBufs][kHeadDim * kVRow];
-  __shared__ int32_t ids[kTile];
-  __shared__ int32_t keys[kTile];
-  __shared__ int32_t run_start[kTile + 1];
+  __shared__ int32_t ids[TILE];
+  __shared__ int32_t keys[TILE];
+  __shared__ int32_t run_start[TILE + 1];
   __shared__ uint64_t bmask[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t total = *offset_total;
-  const int64_t e0 = (int64_t)blockIdx.x * kTile;
+  const int64_t e0 = (int64_t)blockIdx.x * TILE;
   if (e0 >= total) return;
-  const int n = (int)min((int64_t)kTile, total - e0);
+  const int n = (int)min((int64_t)TILE, total - e0);
   const int Hq = G * Hpg;
   const int epr = 32 / Hpg;  // entries per 32-row tile
   int32_t mykey = -1;
@@ -819,8 +823,8 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
 // the block are masked, the local block gets the causal mask. Then each row folds in
 // the partials (o / l, m, l) of its rare entries, computed by the reverse-index path, in
 // slot order, and the final output is written. No partial is stored for shared entries.
-template <class E>
-__global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
+template <class E, int NW = 8>
+__global__ __launch_bounds__(64 * NW, 1) void qtile_attn_kernel(
     const typename E::elem* __restrict__ Q, const typename E::elem* __restrict__ K,
     const typename E::elem* __restrict__ V, const int32_t* __restrict__ block_idx,
     const int32_t* __restrict__ shared, const typename E::elem* __restrict__ part_o,
@@ -838,7 +842,7 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int epr = 32 / Hpg;
-  const int QT = 8 * epr;
+  const int QT = NW * epr;
   const int64_t tile = blockIdx.x / G;
   const int g = (int)(blockIdx.x % G);
   const int64_t i0 = tile * QT;
@@ -849,7 +853,7 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
   __syncthreads();
   int ns = 0;
   while (ns < top_k && sl[ns] >= 0) ++ns;
-  for (int tok = tid; tok < ntok; tok += 512) {
+  for (int tok = tid; tok < ntok; tok += 64 * NW) {
     const int32_t* tl = block_idx + ((i0 + tok) * G + g) * top_k;
     const int b = (int)((q_begin + i0 + tok) / kBlock);
     uint64_t mk = 0;
@@ -879,7 +883,7 @@ __global__ __launch_bounds__(512, 1) void qtile_attn_kernel(
   float m_r[1] = {-INFINITY}, l_r[1] = {0.f};
   f32x16 o[1][4] = {};
 
-  KvStage<E, 512> st;
+  KvStage<E, 64 * NW> st;
   if (ns > 0) {
     st.load(K, V, g, sl[0], seq_len, tid);
     st.store(Ks[0], Vt[0], tid);
@@ -1500,9 +1504,9 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
                        (const uint16_t*)k, (const uint16_t*)v, block_idx, sorted, offset + nb,
                        (uint16_t*)part_o, part_ml, G, Hpg, top_k, q_begin, seq_len);
   else
-    hipLaunchKernelGGL((kv_attn_kernel<E>), dim3(tiles), dim3(256), 0, st, (const elem*)q,
-                       (const elem*)k, (const elem*)v, block_idx, sorted, offset + nb, part_o,
-                       part_ml, G, Hpg, top_k, q_begin, seq_len);
+    hipLaunchKernelGGL((kv_attn_kernel<E, kTileF32>), dim3((unsigned)((n_entries + kTileF32 - 1) / kTileF32)),
+                       dim3(256), 0, st, (const elem*)q, (const elem*)k, (const elem*)v, block_idx,
+                       sorted, offset + nb, part_o, part_ml, G, Hpg, top_k, q_begin, seq_len);
   if constexpr (E::is_bf16) {
     if (top_k <= 16)
       hipLaunchKernelGGL((qtile_attn_bf16_kernel<16>), dim3((unsigned)npairs), dim3(512), 0, st,
@@ -1518,7 +1522,8 @@ static hipError_t launch_kv_t(const void* q, const void* k, const void* v,
                          q_begin, q_count, seq_len);
   }
   if constexpr (!E::is_bf16)
-    hipLaunchKernelGGL((qtile_attn_kernel<E>), dim3((unsigned)npairs), dim3(512), 0, st,
+    hipLaunchKernelGGL((qtile_attn_kernel<E, kQtileWavesF32>), dim3((unsigned)npairs),
+                       dim3(64 * kQtileWavesF32), 0, st,
                        (const elem*)q, (const elem*)k, (const elem*)v, block_idx, shared,
                        (const elem*)part_o, part_ml, (elem*)out, lse, G, Hpg, top_k, q_begin,
                        q_count, seq_len);

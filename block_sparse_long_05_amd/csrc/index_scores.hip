@@ -14,6 +14,8 @@
 // blocks for up to 16 groups at a time on 16x16 MFMAs, K operands loaded straight
 // from global memory into registers (16 B per lane, all 32 loads of a block issued
 // before the first MFMA).
+#include <algorithm>
+
 #include "msa_device.h"
 #include "msa_launch.h"
 
@@ -69,8 +71,14 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_kernel(
   // Heaviest (latest) rows first: causal work grows with the row's position.
   const int64_t r0 = ((int64_t)gridDim.x - 1 - blockIdx.x) * 256;
   const int64_t r_last = min(r0 + 255, nrows - 1);
-  const int cmax = (int)((q_begin + r_last / G) / kBlock);
-  if (cmax < top_k) return;  // every row keeps all its visible blocks: nothing to score
+  const int cmax_rows = (int)((q_begin + r_last / G) / kBlock);
+  if (cmax_rows < top_k) return;  // every row keeps all its visible blocks: nothing to score
+  // this workgroup's key blocks: chunk blockIdx.y of gridDim.y (block scores are independent,
+  // so small problems spread a row tile's blocks over several workgroups)
+  const int per = (cmax_rows + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int c_lo = (int)blockIdx.y * per;
+  const int cmax = min(cmax_rows, c_lo + per);
+  if (c_lo >= cmax) return;
 
   // This lane's B operands (index query rows), two 32-row tiles per wave.
   op_t qop[2][C::kNStep];
@@ -119,10 +127,10 @@ __global__ __launch_bounds__(256, 2) void index_scores_prefill_kernel(
     }
   };
 
-  load_block(0);
-  store_block(0);
+  load_block(c_lo);
+  store_block(c_lo & 1);
   __syncthreads();
-  for (int c = 0; c < cmax; ++c) {
+  for (int c = c_lo; c < cmax; ++c) {
     const bool has_next = c + 1 < cmax;
     if (has_next) load_block(c + 1);
     const elem* kb = lds + (c & 1) * C::kBuf + (lane & 31) * C::kRow + (lane >> 5) * E::kPerLane;
@@ -620,8 +628,13 @@ static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, float* 
     return hipGetLastError();
   }
   const int64_t grid = (rows + 255) / 256;
+  // enough workgroups for the chip (about 1024): the heaviest row tiles' blocks are split
+  // into up to nblk / 2 chunks
+  int64_t chunks = (1024 + grid - 1) / grid;
+  chunks = std::max<int64_t>(1, std::min<int64_t>(chunks, (nblk + 1) / 2));
   const size_t lds = 2 * C::kBuf * sizeof(typename E::elem);
-  hipLaunchKernelGGL((index_scores_prefill_kernel<E, DI>), dim3((unsigned)grid), dim3(256), lds,
+  hipLaunchKernelGGL((index_scores_prefill_kernel<E, DI>), dim3((unsigned)grid, (unsigned)chunks),
+                     dim3(256), lds,
                      st, (const typename E::elem*)q_idx, (const typename E::elem*)k_idx, bs,
                      q_begin, q_count, G, top_k, nblk);
   return hipGetLastError();
