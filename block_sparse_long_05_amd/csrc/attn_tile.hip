@@ -1064,32 +1064,17 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   const int64_t i0 = tile * QT;
   const int ntok = (int)min((int64_t)QT, q_count - i0);
   const int Hq = G * Hpg;
-  // the shared list (ascending, -1 padded): each wave counts it from one load per lane
-  const int slv = lane < top_k ? shared[(tile * G + g) * top_k + lane] : -1;
-  const int ns = __popcll(__ballot(slv >= 0));
-  if (tid < 64) sl[tid] = slv;  // -1 past the list
-  if (tid < QT) {
-    selmask[tid] = 0ull;
-    raremask[tid] = 0ull;
-  }
-  __syncthreads();
-  // Per token: bit j of selmask = it keeps shared block j, bit s of raremask = its slot s
-  // is visible and not shared. One thread per kept entry (coalesced id loads).
-  for (int en = tid; en < ntok * top_k; en += 512) {
-    const int tk = en / top_k;
-    const int s2 = en - tk * top_k;
-    const int c = block_idx[((i0 + tk) * G + g) * top_k + s2];
-    const int b = (int)((q_begin + i0 + tk) / kBlock);
-    if (c < 0 || c > b) continue;
-    int jm = -1;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) jm = sl[j] == c ? j : jm;  // c >= 0 never meets the -1s
-    if (jm >= 0)
-      atomicOr(&selmask[tk], 1ull << jm);
-    else
-      atomicOr(&raremask[tk], 1ull << s2);
-  }
-
+  // The loads that depend only on the launch go out together and share one round trip: the
+  // tile's shared list (ascending, -1 padded; each wave counts it from one load per lane),
+  // this thread's first kept entry id and the lane's query row. The barriers below wait for
+  // LDS only, so the query rows stay in flight across them.
+  // Every load is unconditional (clamped indexes, results selected afterwards): loads behind
+  // lane conditions would leave the compiler unable to count them, and it would then wait for
+  // all of them at the first use of any.
+  const int slv_raw = shared[(tile * G + g) * top_k + min(lane, top_k - 1)];
+  const int ne = ntok * top_k;
+  const int en0 = min(tid, ne - 1);
+  const int c_first = block_idx[((i0 + en0 / top_k) * G + g) * top_k + en0 % top_k];
   const float qk_scale = kLog2e / sqrtf((float)kHeadDim);
   const int n32 = lane & 31, q = lane >> 5;
   const int e = n32 / Hpg;
@@ -1099,20 +1084,53 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   const int64_t irow = i0 + (ok ? tok : 0);
   const int64_t t = q_begin + irow;
   const int tq = (int)t;
+  // a lane without a token reads its tile's first row: its results are never stored
   T::qop_t qop[T::kQSteps];
-  T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, ok);
-  __syncthreads();
+  T::load_q(qop, Q + (t * Hq + (int64_t)g * Hpg + h) * kHeadDim, q, true);
+  const int slv = lane < top_k ? slv_raw : -1;
+  const int ns = __popcll(__ballot(slv >= 0));
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // the first shared block (lane 0's list entry) is staged while the masks are built
+  if (ns > 0) {
+    const int c0 = __builtin_amdgcn_readfirstlane(slv);
+    k_block_dma_asm<512>(K, g, c0, seq_len, Kb0, wv, dma_lane_off<false>(lane), tid);
+    k_block_dma_asm<512, true>(V, g, c0, seq_len, Vb0, wv, dma_lane_off<true>(lane), tid);
+  }
+  if (tid < 64) sl[tid] = slv;  // -1 past the list
+  if (tid < QT) {
+    selmask[tid] = 0ull;
+    raremask[tid] = 0ull;
+  }
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    MSA_WAIT_VMCNT_LDS(63);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  lds_barrier();
+  // Per token: bit j of selmask = it keeps shared block j, bit s of raremask = its slot s
+  // is visible and not shared. One thread per kept entry (coalesced id loads).
+  auto mark = [&](int en, int c) __attribute__((always_inline)) {
+    const int tk = en / top_k;
+    const int s2 = en - tk * top_k;
+    const int b = (int)((q_begin + i0 + tk) / kBlock);
+    if (c < 0 || c > b) return;
+    int jm = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) jm = sl[j] == c ? j : jm;  // c >= 0 never meets the -1s
+    if (jm >= 0)
+      atomicOr(&selmask[tk], 1ull << jm);
+    else
+      atomicOr(&raremask[tk], 1ull << s2);
+  };
+  if (tid < ne) mark(tid, c_first);
+  for (int en = tid + 512; en < ne; en += 512) mark(en, block_idx[((i0 + en / top_k) * G + g) * top_k + en % top_k]);
+  lds_barrier();
   const uint64_t mymask = ok ? selmask[tok] : 0ull;
   const uint64_t myrare = ok ? raremask[tok] : 0ull;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4] = {};
 
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  if (ns > 0) {
-    const int c0 = __builtin_amdgcn_readfirstlane(sl[0]);
-    k_block_dma_s<512>(K, g, c0, seq_len, Kb0, wv, dma_lane_off<false>(lane), tid);
-    k_block_dma_s<512, true>(V, g, c0, seq_len, Vb0, wv, dma_lane_off<true>(lane), tid);
-  }
   // Rare partials first, while the first shared block is being staged: one pass reads each
   // rare slot's (m, l) and partial (lane-interleaved entry blocks, as the tile kernel wrote
   // them: each load instruction covers whole cache lines) and merges it into the row's
@@ -1129,7 +1147,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
         buffer_view(part_o + ebase * Hpg * kHeadDim, span * Hpg * kHeadDim * 2);
     const uint32_t tok_e = (uint32_t)((ok ? tok : 0) * G * top_k);
     // slots whose (m, l) and partial loads are issued together
-    constexpr int kPartPer = 2;
+    constexpr int kPartPer = 3;
     const uint32_t lane_b = (uint32_t)(8 * (h + Hpg * q)) * 2;
     for (uint64_t rem = myrare; __ballot(rem != 0);) {
       float2 ml[kPartPer];
@@ -1195,28 +1213,39 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const int n32v = lane_v & 31, qv = lane_v >> 5;
     if (j + 1 < ns) {
       const int cn = __builtin_amdgcn_readfirstlane(sl[j + 1]);
-      k_block_dma_s<512>(K, g, cn, seq_len, Kn, wv, dma_lane_off<false>(lane_v), tid_v);
-      k_block_dma_s<512, true>(V, g, cn, seq_len, Vn, wv, dma_lane_off<true>(lane_v), tid_v);
+      k_block_dma_asm<512>(K, g, cn, seq_len, Kn, wv, dma_lane_off<false>(lane_v), tid_v);
+      k_block_dma_asm<512, true>(V, g, cn, seq_len, Vn, wv, dma_lane_off<true>(lane_v), tid_v);
     }
     const bool sel = (mymask >> j) & 1ull;
     if (__ballot(sel) == 0) return;
-    // last visible key offset in the block (int32: t < 2^31), -1 when the row did not keep
-    // it; rows without a token (ok false) are never stored and need no mask
+    // A row that did not keep the block (or has no token) joins the products but takes the
+    // exponent offset -inf: its probabilities are all 0 and its maximum is ignored, with no
+    // mask on its single scores. Only a block that reaches past a keeping row's own position
+    // (the causal block of the query tile) masks single scores: one uniform test per block.
+    // lim: last visible key offset in the block (int32: t < 2^31).
     const int lim = min(max(tq - c * kBlock, -1), kBlock - 1);
-    const int lime = sel ? lim : -1;
-    // one uniform test per block: most shared blocks are fully visible to every row of the
-    // wave, and then the scores go to the softmax without a compare and select each
-    const bool masked = __ballot(ok && lime < kBlock - 1) != 0;
-    int limq = lime - 4 * qv;  // the lane's key offset 4q folded into the limit
+    const bool masked = __ballot(sel && lim < kBlock - 1) != 0;
+    int limq = lim - 4 * qv;  // the lane's key offset 4q folded into the limit
     asm volatile("" : "+v"(limq));
     // the block's 128 keys: all four S^T tiles and their maximum first (one test of the lazy
     // maximum per block), then per 64-key half the exponentials, which the compiler can
     // interleave with the other half's PV products
     float p[4][16];
     float mx = -INFINITY;
+    f32x16 acc4[4] = {};
+    {
+      const uint8_t* kr = Kc + n32v * 256;
+#pragma unroll
+      for (int s = 0; s < kHeadDim / 16; ++s) {
+        const int pos = (2 * s + qv) ^ (n32v & 15);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          acc4[kt] = mfma32(*reinterpret_cast<const u32x4*>(kr + kt * 32 * 256 + pos * 16), qop[s], acc4[kt]);
+      }
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const f32x16 sv = s_tile_swz(Kc, 32 * kt + n32v, qop, qv);
+      const f32x16 sv = acc4[kt];
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -1230,7 +1259,7 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mxs = mx * qk_scale;
-    const bool raise = mxs > m_run + 8.f;  // false while the row has no score (-inf)
+    const bool raise = sel && mxs > m_run + 8.f;
     if (__ballot(raise)) {
       const float alpha = raise ? fast_exp2(m_run - mxs) : 1.f;
       m_run = raise ? mxs : m_run;
@@ -1240,7 +1269,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
-    const float mneg = m_run == -INFINITY ? 0.f : -m_run;  // masked scores give exp2(-inf) = 0
+    // masked scores and rows that skip the block give exp2(-inf) = 0
+    const float mneg = !sel ? -INFINITY : m_run == -INFINITY ? 0.f : -m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -1263,10 +1293,13 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     lsum += __shfl_xor(lsum, 32, 64);
     l_run += lsum;
   };
+#pragma unroll
+  for (int s2 = 0; s2 < T::kQSteps; ++s2) asm volatile("" ::"v"(qop[s2]));
   for (int j = 0; j < ns; j += 2) {
     shared_block(j, Kb0, Vb0, Kb1, Vb1);
     if (j + 1 < ns) shared_block(j + 1, Kb1, Vb1, Kb0, Vb0);
   }
+  MSA_WAIT_VMCNT(0);
 
   if (ok) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;

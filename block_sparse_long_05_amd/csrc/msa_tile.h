@@ -72,6 +72,59 @@ __device__ __forceinline__ void k_block_dma_s(const uint16_t* K, int g, int c, i
   }
 }
 
+// ---- the same staging issued as inline assembly --------------------------------------------
+// The compiler does not track these loads, so it adds no waits for them. (Its tracking of the
+// direct-to-LDS builtin cannot tell the buffers of a ring apart: with a load into one buffer in
+// flight it drains every pending load before LDS reads of another buffer, which serialises a
+// double buffer.) The caller owns the synchronisation: MSA_WAIT_VMCNT on this wave's loads
+// (kBlock * 256 / 1024 / (NT / 64) per block), then a barrier, before any wave reads the
+// buffer, and no wave may still read a buffer when a load into it is issued. Loads issued
+// before an ordinary load complete before it (vector memory loads return in order), so the
+// compiler's own waits stay correct. M0 holds the wave-uniform LDS address of the 1 KiB row
+// group (the load writes lane l's 16 bytes at M0 + 16 l).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+// `gbase` and `lds` must be wave-uniform; they are moved to scalar registers explicitly (the
+// compiler cannot always prove a value uniform, and the instruction takes its base there).
+__device__ __forceinline__ void lds_dma16(const uint8_t* gbase, uint32_t voff, uint32_t lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)gbase;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint8_t* sbase = (const uint8_t*)(uintptr_t)(lo | (hi << 32));
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0)
+               : "memory");
+}
+
+template <int NT, bool kVSwz = false>
+__device__ __forceinline__ void k_block_dma_asm(const uint16_t* K, int g, int c, int64_t seq_len,
+                                                uint8_t* kbuf, int wave, uint32_t lane_off,
+                                                int tid) {
+  constexpr int kPer = kBlock * 256 / 1024 / (NT / 64);  // 1 KiB loads per wave
+  const int64_t key0 = (int64_t)c * kBlock;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(K + ((int64_t)g * seq_len + key0) * kHeadDim);
+  const uint32_t lds = lds_addr(kbuf) + (uint32_t)(wave * kPer * 1024);
+  if (seq_len - key0 < kBlock) {
+    // the sequence's last block: rows past its end repeat a valid row
+    const int nk = (int)(seq_len - key0);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int li = wave * kPer + i;
+      const int r = 4 * li + (lane >> 4);
+      const int chunk = (lane & 15) ^ (kVSwz ? v_swz(r) : (r & 15));
+      const int rr = r < nk ? r : nk - 1;
+      lds_dma16(kg, (uint32_t)(rr * kHeadDim + chunk * 8) * 2u, lds + 1024 * i);
+    }
+    return;
+  }
+  const uint8_t* base = kg + (size_t)wave * kPer * 1024;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    lds_dma16(base, 1024u * i + (lane_off ^ (uint32_t)((kVSwz ? 16 : 64) * (i & 3))), lds + 1024 * i);
+}
+
 __device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q) {
   f32x16 acc = {};
 #pragma unroll
