@@ -113,23 +113,33 @@ __global__ __launch_bounds__(256, 2) void kl_stats_unit_kernel(
     const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
     u32x4 qiop[kHeadDim / 16];
     load_row_op(qiop, QI + (t * G + g) * kHeadDim, q);
-    for (int h = kIndexOnly ? Hpg : 0; h <= Hpg; ++h) {
-      u32x4 qop[kHeadDim / 16];
-      if (h < Hpg) load_row_op(qop, qrow + h * kHeadDim, q);
-      const float sc = h < Hpg ? c_main : c_idx;
+    // (max, sum) of head h's scores (h < Hpg, from the rows in qop) or of the index scores
+    // only entries of the block's own tokens see part of it: a wave with none of those skips
+    // the per-score causal compares (a lane without entry has limit -1024)
+    const bool cut = __ballot(limq < kBlock - 1 - 4 * q) != 0;
+    auto stat = [&](int h, const u32x4* qop, bool main) __attribute__((always_inline)) {
+      const float sc = main ? c_main : c_idx;
       f32x16 sv[4];
       float mx = -INFINITY;
       int lq = limq;
       asm volatile("" : "+v"(lq));
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        sv[kt] = h < Hpg ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
-                         : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
+        sv[kt] = main ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
+                      : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
+        if (cut) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? sv[kt][r] * sc : -INFINITY;
-          sv[kt][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r) {
+            const float x = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? sv[kt][r] * sc : -INFINITY;
+            sv[kt][r] = x;
+            mx = fmaxf(mx, x);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sv[kt][r] *= sc;
+            mx = fmaxf(mx, sv[kt][r]);
+          }
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -142,7 +152,22 @@ __global__ __launch_bounds__(256, 2) void kl_stats_unit_kernel(
       if (ok && q == 0)
         *reinterpret_cast<float2*>(part_stats + ((int64_t)id * (Hpg + 1) + h) * 2) =
             make_float2(mx, l);
+    };
+    if constexpr (!kIndexOnly) {
+      // the next head's query rows are loaded while this head's products run (two buffers;
+      // past the last head the last one is loaded again: every load is unconditional)
+      const int hl = Hpg - 1;
+      u32x4 qa[kHeadDim / 16], qb[kHeadDim / 16];
+      load_row_op(qa, qrow, q);
+      for (int h = 0; h < Hpg; h += 2) {
+        load_row_op(qb, qrow + min(h + 1, hl) * kHeadDim, q);
+        stat(h, qa, true);
+        if (h + 1 >= Hpg) break;
+        load_row_op(qa, qrow + min(h + 2, hl) * kHeadDim, q);
+        stat(h + 1, qb, true);
+      }
     }
+    stat(Hpg, qiop, false);
   }
 }
 
@@ -208,11 +233,15 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) w[kt][r] = 0.f;
-    // P: mean over the group's heads of each head's probabilities
-    for (int h = 0; h < Hpg; ++h) {
-      u32x4 qop[kHeadDim / 16];
-      load_row_op(qop, qrow + h * kHeadDim, q);
-      const float lh = lrow[h];  // a lane without entry reads row 0 (all its keys masked)
+    // P: mean over the group's heads of each head's probabilities. The next head's query
+    // rows and log-sum-exp are loaded while this head's products run (two buffers; past the
+    // last head the last one is loaded again, so every load is unconditional and the compiler
+    // waits only for the buffer it reads).
+    // Only entries of the block's own tokens see part of it (their local block); a wave with
+    // none of those skips the per-score causal compares (one uniform test per wave). A lane
+    // without entry has every key masked: its limit is -1024.
+    const bool cut = __ballot(limq < kBlock - 1 - 4 * q) != 0;
+    auto head_p = [&](const u32x4* qop, float lh) __attribute__((always_inline)) {
       // the causal compares are redone per head (two VALU ops per score) rather than
       // kept as 64 hoisted lane masks, which the compiler would spill
       int lq = limq;
@@ -220,11 +249,31 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
+        if (cut) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(sv[r], c_main, -lh));
-          w[kt][r] += 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? e : 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(fmaf(sv[r], c_main, -lh));
+            w[kt][r] += 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? e : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[kt][r] += fast_exp2(fmaf(sv[r], c_main, -lh));
         }
+      }
+    };
+    {
+      const int hl = Hpg - 1;
+      u32x4 qa[kHeadDim / 16], qb[kHeadDim / 16];
+      load_row_op(qa, qrow, q);
+      float la = lrow[0];  // a lane without entry reads row 0 (all its keys masked)
+      for (int h = 0; h < Hpg; h += 2) {
+        load_row_op(qb, qrow + min(h + 1, hl) * kHeadDim, q);
+        const float lb = lrow[min(h + 1, hl)];
+        head_p(qa, la);
+        if (h + 1 >= Hpg) break;
+        load_row_op(qa, qrow + min(h + 2, hl) * kHeadDim, q);
+        la = lrow[min(h + 2, hl)];
+        head_p(qb, lb);
       }
     }
     const float inv_h = 1.f / (float)Hpg;
@@ -242,7 +291,12 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
         const float iv = fast_exp2(z);
         // P ln(P / I) in log2 units; p = 0 gives 0 (the clamp only keeps the log finite)
         lsum += p * (__builtin_amdgcn_logf(fmaxf(p, 1e-30f)) - z);
-        w[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? index_scale * (iv - p) : 0.f;
+        w[kt][r] = index_scale * (iv - p);
+      }
+      if (cut) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          w[kt][r] = 32 * kt + 8 * (r >> 2) + (r & 3) <= lq ? w[kt][r] : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) wp[kt][i] = pack_bf16x2(w[kt][2 * i], w[kt][2 * i + 1]);
