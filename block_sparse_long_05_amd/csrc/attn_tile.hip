@@ -751,9 +751,11 @@ __global__ __launch_bounds__(256, 2) void kv_attn_bf16_kernel(
       // so the maximum is exact and the accumulator is never rescaled
       float p[4][16];
       float mx = -INFINITY;
+      f32x16 acc4[4];
+      s_tiles4_swz(Kb, n32v, qc, qv, acc4);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32v, qc, qv);
+        const f32x16 sv = acc4[kt];
         // the compare and select only where a row of the wave ends inside the block
         if (masked) {
 #pragma unroll
@@ -1232,17 +1234,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     // interleave with the other half's PV products
     float p[4][16];
     float mx = -INFINITY;
-    f32x16 acc4[4] = {};
-    {
-      const uint8_t* kr = Kc + n32v * 256;
-#pragma unroll
-      for (int s = 0; s < kHeadDim / 16; ++s) {
-        const int pos = (2 * s + qv) ^ (n32v & 15);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          acc4[kt] = mfma32(*reinterpret_cast<const u32x4*>(kr + kt * 32 * 256 + pos * 16), qop[s], acc4[kt]);
-      }
-    }
+    f32x16 acc4[4];
+    s_tiles4_swz(Kc, n32v, qop, qv, acc4);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const f32x16 sv = acc4[kt];

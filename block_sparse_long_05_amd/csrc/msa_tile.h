@@ -135,6 +135,23 @@ __device__ __forceinline__ f32x16 s_tile_swz(const uint8_t* kbuf, int m, const u
   return acc;
 }
 
+// The four S^T tiles of a 128-key block (keys 32 kt + m for lane column m) as four interleaved
+// MFMA chains: each k-step's operand reads feed four independent accumulators, so the
+// matrix core does not wait on one chain's results between tiles.
+__device__ __forceinline__ void s_tiles4_swz(const uint8_t* kbuf, int m, const u32x4* qop, int q,
+                                             f32x16 (&acc)[4]) {
+  const uint8_t* kr = kbuf + m * 256;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < kHeadDim / 16; ++s) {
+    const int pos = (2 * s + q) ^ (m & 15);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      acc[kt] = mfma32(*reinterpret_cast<const u32x4*>(kr + kt * 32 * 256 + pos * 16), qop[s], acc[kt]);
+  }
+}
+
 // O^T += V^T . P^T over one 64-key half of the block, V row-major in LDS in the V
 // row swizzle of k_block_dma. The LDS transpose read (ds_read_b64_tr_b16) hands
 // lane i of a 16-lane group column i % 4 of the 8-byte rows that lanes 4 j + i / 4
