@@ -500,15 +500,18 @@ __global__ __launch_bounds__(256) void index_scores_decode_kernel(
 }
 
 // Decode, bf16 with index dim 128 and up to 16 groups: each wave streams its blocks
-// through a private ring of 4 LDS stages of 32 keys (8 KiB each) filled by direct
-// global->LDS loads, with three stages in flight while one is consumed. A quarter-wave
+// through a private ring of 2 LDS stages of 32 keys (8 KiB each) filled by direct
+// global->LDS loads, one stage in flight while the other is consumed. With 64 KiB per
+// workgroup two workgroups share a CU, which covers one's start and end with the other's
+// stream (4 x 131072 keys: 25 -> 21 us; 8 x 1M stays at 311 us, 6.9 TB/s, with 2 to 5
+// stages). A quarter-wave
 // loads one whole 256-byte key row, so the reads are fully coalesced; the 16-byte
 // chunks of row r are stored XOR-swizzled (position p holds chunk p ^ (r % 16)), so
 // the MFMA operand reads - 16 rows, one chunk each per quarter-wave - fall in distinct
 // LDS banks.
 constexpr int kScanKeys = 32;                     // keys per stage
 constexpr int kScanStage = kScanKeys * 256;       // bytes per stage (bf16, d = 128)
-constexpr int kScanRing = 4;                      // stages per wave
+constexpr int kScanRing = 2;                      // stages per wave
 constexpr int kScanLoads = kScanKeys / 4;         // 1 KiB loads per stage
 
 __device__ __forceinline__ void scan_issue_stage(const uint16_t* rows, uint8_t* stage_lds,
@@ -531,7 +534,7 @@ __global__ __launch_bounds__(256) void index_scores_decode_lds_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     float* __restrict__ block_scores, const int32_t* __restrict__ seq_lens, int64_t max_len,
     int G, int top_k, int nblk, int blocks_per_wg, PageMap pm) {
-  __shared__ __align__(16) uint8_t lds[4][kScanRing][kScanStage];  // 128 KiB
+  __shared__ __align__(16) uint8_t lds[4][kScanRing][kScanStage];  // 64 KiB: two workgroups a CU
   constexpr int kPerBlock = kBlock / kScanKeys;                      // stages per block
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
