@@ -1038,6 +1038,8 @@ __global__ __launch_bounds__(64 * NW, 1) void qtile_attn_kernel(
 // per-token masks), and each lane folds in its own rare partials through buffer views,
 // before the shared blocks, in one online pass with the same lazy maximum: their loads
 // overlap the first block's staging.
+// Launch bounds (512, 2): at least two waves per SIMD, i.e. 256 registers a lane; the 135 KiB
+// of LDS let one workgroup occupy a CU.
 template <int KMAX>
 __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -1046,9 +1048,8 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
     const float* __restrict__ part_ml, uint16_t* __restrict__ out, float* __restrict__ lse,
     int G, int Hpg, int top_k, int64_t q_begin, int64_t q_count, int64_t seq_len) {
   typedef TileOps<BF16> T;
-  // two buffers per operand as distinct arrays: with the block loop unrolled by two every
-  // access names its buffer, so the compiler can tell that the loads of block j + 1 do
-  // not alias the reads of block j (and does not wait for them)
+  // two buffers per operand: block j + 1 is staged while block j is read (the block loop is
+  // unrolled by two, so every access names its buffer)
   __shared__ __align__(16) uint8_t Kb0[kBlock * 256];
   __shared__ __align__(16) uint8_t Kb1[kBlock * 256];
   __shared__ __align__(16) uint8_t Vb0[kBlock * 256];
@@ -1069,10 +1070,10 @@ __global__ __launch_bounds__(512, 2) void qtile_attn_bf16_kernel(
   // The loads that depend only on the launch go out together and share one round trip: the
   // tile's shared list (ascending, -1 padded; each wave counts it from one load per lane),
   // this thread's first kept entry id and the lane's query row. The barriers below wait for
-  // LDS only, so the query rows stay in flight across them.
-  // Every load is unconditional (clamped indexes, results selected afterwards): loads behind
-  // lane conditions would leave the compiler unable to count them, and it would then wait for
-  // all of them at the first use of any.
+  // LDS only, so the query rows stay in flight across them. Every load is unconditional
+  // (clamped indexes, results selected afterwards): loads behind lane conditions would leave
+  // the compiler unable to count them, and it would then wait for all of them at the first
+  // use of any.
   const int slv_raw = shared[(tile * G + g) * top_k + min(lane, top_k - 1)];
   const int ne = ntok * top_k;
   const int en0 = min(tid, ne - 1);
