@@ -376,3 +376,90 @@ def test_topk_long_rows_decode(nblk_max):
         for g in range(G):
             sel, _ = orc.select_blocks(s[b, g, :blocal].double().numpy(), blocal, top_k)
             assert got[b, g].tolist() == sel.tolist(), (b, g)
+
+
+def _sweep_prefill_cases(n=16, seed=2027):
+    """Seeded random configurations beyond the hand-picked cases: head counts 1..16 (rows
+    of a 32-row query tile left unused), top_k 1..40, ragged lengths, both index dims, the
+    fused and the separate index branch, and chunks with odd starts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hpg = int(rng.choice([1, 2, 4, 5, 6, 7, 9, 12, 16]))
+        g = int(rng.integers(1, max(2, 33 // (hpg * 4)) + 1))
+        t = int(rng.integers(600, 6200))
+        k = int(rng.choice([1, 2, 3, 5, 7, 11, 16, 20, 33, 40]))
+        d_idx = int(rng.choice([64, 128]))
+        planted = int(rng.integers(0, 5))
+        index = "fused" if (k <= 16 and rng.random() < 0.5) else "separate"
+        q0 = int(rng.integers(0, t // 2)) | 1 if rng.random() < 0.4 else 0
+        qn = t - q0 if q0 == 0 else int(rng.integers(1, t - q0 + 1))
+        algo = str(rng.choice(["auto", "query_centric"]))
+        cases.append((i, t, g, hpg, d_idx, k, planted, index, q0, qn, algo))
+    return cases
+
+
+@pytest.mark.parametrize("i,T,G,Hpg,d_idx,top_k,planted,index,q0,qn,algo",
+                         _sweep_prefill_cases())
+def test_prefill_sweep(i, T, G, Hpg, d_idx, top_k, planted, index, q0, qn, algo):
+    x = synth.prefill_inputs(T, G, Hpg, 128, d_idx, dtype="bf16", seed=1000 + i,
+                             planted_per_group=planted)
+    print(f"prefill sweep {i}: T={T} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k} "
+          f"index={index} rows [{q0}, {q0 + qn}) {algo}", flush=True)
+    xd = _to(x)
+    out = torch.zeros_like(xd["q"])
+    lse = torch.full(xd["q"].shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    out, idx, bs = msa.prefill(xd, top_k, q_begin=q0, q_count=qn, algo=algo, out=out, lse=lse,
+                               index=index)
+    torch.cuda.synchronize()
+    rows = np.arange(q0, q0 + qn)
+    res = orc.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], top_k, rows=rows)
+    out, lse = parity.np32(out), parity.np32(lse)
+    info = parity.check_prefill(x, rows, out, idx.cpu().numpy(),
+                                None if bs is None else parity.np32(bs), res, top_k,
+                                q_begin=q0, label=f"sweep {i}", lse_gpu=lse)
+    assert np.all(out[:q0] == 0) and np.all(out[q0 + qn:] == 0)
+    assert np.isnan(lse[:q0]).all() and np.isnan(lse[q0 + qn:]).all()
+    print(info)
+
+
+def _sweep_decode_cases(n=16, seed=4099):
+    """Seeded random decode steps: ragged lengths (one-token caches, lengths on and next to
+    block edges), group counts on both sides of the scan kernels' 16-group limit, head
+    counts 1..16, top_k 1..64, both index dims and both dtypes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        b = int(rng.integers(1, 7))
+        cap = int(rng.integers(200, 20000))
+        lens = []
+        for _ in range(b):
+            r = rng.random()
+            if r < 0.15:
+                lens.append(1)
+            elif r < 0.35:
+                lens.append(min(cap, 128 * int(rng.integers(1, cap // 128 + 1)) + int(rng.integers(-1, 2))))
+            else:
+                lens.append(int(rng.integers(1, cap + 1)))
+        lens = [max(1, x) for x in lens]
+        lens[int(rng.integers(0, b))] = cap
+        g = int(rng.choice([1, 2, 4, 8, 12, 16, 20]))
+        hpg = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        k = int(rng.choice([1, 2, 4, 7, 16, 33, 64]))
+        d_idx = int(rng.choice([64, 128]))
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        planted = int(rng.integers(0, 5))
+        cases.append((i, b, cap, lens, g, hpg, d_idx, k, dtype, planted))
+    return cases
+
+
+@pytest.mark.parametrize("i,B,cap,lens,G,Hpg,d_idx,top_k,dtype,planted", _sweep_decode_cases())
+def test_decode_sweep(i, B, cap, lens, G, Hpg, d_idx, top_k, dtype, planted):
+    x = synth.decode_inputs(B, cap, G, Hpg, 128, d_idx, dtype=dtype, seed=2000 + i,
+                            planted_per_group=planted, seq_lens=lens)
+    print(f"decode sweep {i}: B={B} L={lens} G={G} Hpg={Hpg} d_idx={d_idx} k={top_k} {dtype}",
+          flush=True)
+    out, idx, bs = _run_decode(x, top_k)
+    res = orc.decode(x["q"], x["k_cache"], x["v_cache"], x["q_idx"], x["k_idx"], x["seq_lens"],
+                     top_k)
+    print(parity.check_decode(x, out, idx, bs, res, top_k, label=f"decode sweep {i}"))
