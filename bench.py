@@ -504,18 +504,19 @@ def run_decode(name, cfg, args, torch, msa, synth):
 
     timers = {}
 
+    # the step: index scan, then selection + attention + combine in one call (the selection
+    # runs inside the attention launch where that is faster)
     def step(timed):
         if not timed:
             msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
-            msa.msa_block_topk(p, bs, idx)
-            msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx, out, ws)
+            msa.msa_sparse_attn_decode_topk(p, x["q"], x["k_cache"], x["v_cache"], bs, idx, out,
+                                            ws)
             return
         with timers.setdefault("index_scan", KernelTimer(torch)):
             msa.msa_index_scores(p, x["q_idx"], x["k_idx"], bs)
-        with timers.setdefault("block_topk", KernelTimer(torch)):
-            msa.msa_block_topk(p, bs, idx)
-        with timers.setdefault("sparse_attn", KernelTimer(torch)):
-            msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx, out, ws)
+        with timers.setdefault("topk_sparse_attn", KernelTimer(torch)):
+            msa.msa_sparse_attn_decode_topk(p, x["q"], x["k_cache"], x["v_cache"], bs, idx, out,
+                                            ws)
 
     for _ in range(args.warmup):
         step(False)

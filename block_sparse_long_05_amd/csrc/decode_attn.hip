@@ -14,9 +14,12 @@
 // bit-identical from run to run).
 #include "msa_device.h"
 #include "msa_launch.h"
+#include "msa_select.h"
 #include "msa_tile.h"
 
 namespace msa {
+
+static_assert(kSelectMaxBlocks == kRowMax, "the host's row limit is the selection's");
 
 // Rows row0 .. row0 + 31 of a block (rows at or past nvalid repeat row nvalid - 1, which
 // the caller masks) into a 32-row LDS buffer: load i covers buffer rows 4 i .. 4 i + 3, a
@@ -36,12 +39,18 @@ __device__ __forceinline__ void rows32_dma(const uint16_t* blk, int row0, int nv
   }
 }
 
+// kSelect: the workgroup first selects its (sequence, group)'s blocks from the block scores
+// itself (row_select_wg, the code of the decode top-k kernel: the same ids), takes the one
+// of its slot and writes it to block_idx; otherwise it reads its block from block_idx.
+template <bool kSelect>
 __global__ __launch_bounds__(256, 2) void decode_attn_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ block_idx,
+    const float* __restrict__ block_scores, int32_t* __restrict__ idx_out, int nblk,
     const int32_t* __restrict__ seq_lens, int64_t max_len, int G, int Hpg, int top_k,
     PageMap pm, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  // staging: per wave 8 KiB of K then 8 KiB of V; reused for the merge (4 x 16 KiB)
+  // staging: per wave 8 KiB of K then 8 KiB of V; reused for the merge (4 x 16 KiB) and,
+  // before the staging, for the selection's candidates
   __shared__ __align__(16) uint8_t lds[4 * 2 * 32 * 256];
   __shared__ float2 mls[4][32];
 
@@ -54,7 +63,39 @@ __global__ __launch_bounds__(256, 2) void decode_attn_bf16_kernel(
   int64_t L = seq_lens[bseq];
   L = L < 1 ? 1 : (L > max_len ? max_len : L);
   const int blocal = (int)((L - 1) / kBlock);
-  const int c = block_idx[u];
+  // B operand of S^T: column n = head n of the group (columns >= Hpg read head Hpg - 1);
+  // loaded first, so that the loads run under the selection or the block id's load
+  const int n32 = lane & 31, q = lane >> 5;
+  const int Hq = G * Hpg;
+  const uint16_t* qrow = Q + (bseq * Hq + (int64_t)g * Hpg + min(n32, Hpg - 1)) * kHeadDim;
+  u32x4 qop[kHeadDim / 16];
+#pragma unroll
+  for (int s = 0; s < kHeadDim / 16; ++s)
+    qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * q);
+  int c;
+  if constexpr (kSelect) {
+    static_assert(sizeof(lds) >= kRowMax * sizeof(uint64_t), "candidates must fit the staging");
+    __shared__ RowSelectShared sh;
+    const int j = (int)(u - bg * top_k);
+    if (blocal + 1 <= top_k) {  // every visible block is kept
+      c = j <= blocal ? j : -1;
+    } else if (j == top_k - 1) {  // the local block is the largest kept id
+      c = blocal;
+    } else {
+      const int Ksel = top_k - 1;
+      row_select_wg(block_scores + bg * nblk, (nblk & 3) == 0, blocal, Ksel,
+                    reinterpret_cast<uint64_t*>(lds), sh, tid);
+      if (tid < Ksel) {
+        const int cc = sh.sel[tid];
+        if (sel_rank(sh.sel, Ksel, cc) == j) sh.slot_id = cc;
+      }
+      __syncthreads();  // also: every candidate read is done before the staging reuses lds
+      c = sh.slot_id;
+    }
+    if (tid == 0) idx_out[u] = c;
+  } else {
+    c = block_idx[u];
+  }
   float* po = part_o + u * Hpg * kHeadDim;
   if (c < 0 || c > blocal) {  // padding or an invisible id: an empty partial
     for (int x = tid; x < Hpg * kHeadDim; x += 256) po[x] = 0.f;
@@ -76,14 +117,6 @@ __global__ __launch_bounds__(256, 2) void decode_attn_bf16_kernel(
   rows32_dma<false>(kblk, 32 * wave, nvalid, Kw, lane);
   rows32_dma<true>(vblk, 32 * wave, nvalid, Vw, lane);
 
-  // B operand of S^T: column n = head n of the group (columns >= Hpg read head Hpg - 1)
-  const int n32 = lane & 31, q = lane >> 5;
-  const int Hq = G * Hpg;
-  const uint16_t* qrow = Q + (bseq * Hq + (int64_t)g * Hpg + min(n32, Hpg - 1)) * kHeadDim;
-  u32x4 qop[kHeadDim / 16];
-#pragma unroll
-  for (int s = 0; s < kHeadDim / 16; ++s)
-    qop[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * q);
   MSA_WAIT_VMCNT(0);
   __builtin_amdgcn_wave_barrier();  // this wave's rows have landed (only this wave reads them)
 
@@ -327,11 +360,20 @@ hipError_t launch_decode_dense_bf16(const void* q, const void* k, const void* v,
 hipError_t launch_decode_attn_bf16(const void* q, const void* k, const void* v,
                                    const int32_t* block_idx, const int32_t* seq_lens, int B,
                                    int64_t max_len, int G, int Hpg, int top_k, PageMap pm,
-                                   float* part_o, float* part_ml, hipStream_t st) {
+                                   float* part_o, float* part_ml, hipStream_t st,
+                                   const float* block_scores, int32_t* idx_out, int nblk) {
   const int64_t units = (int64_t)B * G * top_k;
-  hipLaunchKernelGGL(decode_attn_bf16_kernel, dim3((unsigned)units), dim3(256), 0, st,
+  if (block_scores != nullptr) {
+    hipLaunchKernelGGL(decode_attn_bf16_kernel<true>, dim3((unsigned)units), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                       block_scores, idx_out, nblk, seq_lens, max_len, G, Hpg, top_k, pm,
+                       part_o, part_ml);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(decode_attn_bf16_kernel<false>, dim3((unsigned)units), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
-                     seq_lens, max_len, G, Hpg, top_k, pm, part_o, part_ml);
+                     nullptr, nullptr, 0, seq_lens, max_len, G, Hpg, top_k, pm, part_o,
+                     part_ml);
   return hipGetLastError();
 }
 

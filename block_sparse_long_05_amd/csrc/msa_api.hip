@@ -143,7 +143,8 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q, const void* k,
                                 const void* v, const int32_t* block_idx, void* out,
                                 void* workspace, size_t workspace_bytes, hipStream_t st,
-                                PageMap pm = PageMap{}) {
+                                PageMap pm = PageMap{}, const float* block_scores = nullptr,
+                                int32_t* idx_out = nullptr) {
   const size_t need = decode_ws_bytes(p, dense);
   if (workspace_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(workspace)) return MSA_ERR_INVALID_ARGUMENT;
@@ -165,7 +166,8 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
   if (decode_block_kernel(p, dense)) {
     hipError_t e = launch_decode_attn_bf16(q, k, v, block_idx, p->seq_lens, p->batch,
                                            p->max_len, p->num_groups, p->heads_per_group,
-                                           p->top_k, pm, part_o, part_ml, st);
+                                           p->top_k, pm, part_o, part_ml, st, block_scores,
+                                           idx_out, (int)nblk_of(p));
     if (e != hipSuccess) return MSA_ERR_HIP;
     return hip_status(launch_decode_combine(bf16, part_o, part_ml, out, p->batch,
                                             p->num_groups, p->heads_per_group, nsplit, st));
@@ -377,6 +379,38 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_idx) ||
       !aligned16(out))
     return MSA_ERR_INVALID_ARGUMENT;
+  return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
+                              workspace_bytes, as_stream(stream));
+}
+
+msa_status msa_sparse_attn_decode_topk(const msa_problem* p, const void* q, const void* k_cache,
+                                       const void* v_cache, const float* block_scores,
+                                       int32_t* block_idx, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  msa_status st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_scores) ||
+      !aligned16(block_idx) || !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < decode_ws_bytes(p, false)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  // The attention workgroups select their own blocks when each of them reads a short row
+  // (<= 1024 blocks) or when every workgroup is resident at once (one per (sequence, group,
+  // slot), two per CU); otherwise the selection's reads, repeated by every workgroup of a
+  // row, cost more than the top-k launch they save.
+  const int64_t nblk = nblk_of(p);
+  const int64_t units = (int64_t)p->batch * p->num_groups * p->top_k;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MSA_ERR_HIP;
+  if (decode_block_kernel(p, false) && nblk <= kSelectMaxBlocks &&
+      (nblk <= 1024 || units <= 2 * (int64_t)cus))
+    return run_decode_attention(p, false, q, k_cache, v_cache, nullptr, out, workspace,
+                                workspace_bytes, as_stream(stream), PageMap{}, block_scores,
+                                block_idx);
+  const msa_status s1 = msa_block_topk(p, block_scores, block_idx, stream);
+  if (s1 != MSA_OK) return s1;
   return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
                               workspace_bytes, as_stream(stream));
 }

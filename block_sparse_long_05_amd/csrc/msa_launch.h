@@ -74,12 +74,19 @@ struct GatherParams {
 
 hipError_t launch_gather_attn(const GatherParams& p, hipStream_t stream);
 
+// Longest decode row (blocks) that a workgroup selects from (msa_select.h: kRowMax).
+constexpr int kSelectMaxBlocks = 8192;
+
 // Sparse decode attention, bf16 (decode_attn.hip): one partial per (sequence, group, kept
-// block) into part_o [B * G * top_k][Hpg][128] / part_ml [..][Hpg][2].
+// block) into part_o [B * G * top_k][Hpg][128] / part_ml [..][Hpg][2]. With block_scores
+// (fp32 [B, G, nblk], nblk <= kRowMax) the kernel selects the blocks itself and writes
+// them to idx_out; block_idx is then not read.
 hipError_t launch_decode_attn_bf16(const void* q, const void* k, const void* v,
                                    const int32_t* block_idx, const int32_t* seq_lens, int B,
                                    int64_t max_len, int G, int Hpg, int top_k, PageMap pm,
-                                   float* part_o, float* part_ml, hipStream_t st);
+                                   float* part_o, float* part_ml, hipStream_t st,
+                                   const float* block_scores = nullptr, int32_t* idx_out = nullptr,
+                                   int nblk = 0);
 
 // Dense decode attention, bf16 (decode_attn.hip): one partial per (sequence, group, split of
 // keys_per_split cache keys), nsplit splits per (sequence, group), as dense_decode_plan sets.

@@ -35,8 +35,8 @@ BLOCK = 128
 
 # Every symbol include/msa.h declares.
 EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
-            "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc",
-            "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
+            "msa_sparse_attn_decode", "msa_sparse_attn_decode_topk",
+            "msa_sparse_attn_decode_noalloc", "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
             "msa_index_kl_prefill", "msa_dense_gqa_attn", "msa_workspace_size",
             "msa_status_string", "msa_abi_version"]
 
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_topk.argtypes = [pp, vp, vp, vp, vp]
     lib.msa_sparse_attn_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_decode_topk.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.msa_sparse_attn_decode_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp]
     lib.msa_dense_gqa_attn.argtypes = [pp, vp, vp, vp, vp, vp, sz, vp]
     i32, i64 = ctypes.c_int32, ctypes.c_int64
@@ -90,8 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_abi_version.argtypes = []
     for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
                  "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
-                 "msa_sparse_attn_decode", "msa_sparse_attn_decode_noalloc",
-                 "msa_dense_gqa_attn", "msa_workspace_size",
+                 "msa_sparse_attn_decode", "msa_sparse_attn_decode_topk",
+                 "msa_sparse_attn_decode_noalloc", "msa_dense_gqa_attn", "msa_workspace_size",
                  "msa_index_kl_prefill",
                  "msa_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -230,6 +231,17 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, block_idx, out, work
     _check(load_library().msa_sparse_attn_decode(
         ctypes.byref(p.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_idx), _ptr(out),
         _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode")
+
+
+def msa_sparse_attn_decode_topk(p: Problem, q, k_cache, v_cache, block_scores, block_idx, out,
+                                workspace=None, stream=None):
+    """msa_block_topk and msa_sparse_attn_decode in one call (the selection inside the
+    attention launch where that is faster): block_idx and out as the two calls write them."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_sparse_attn_decode_topk(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_scores),
+        _ptr(block_idx), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+        "msa_sparse_attn_decode_topk")
 
 
 def msa_sparse_attn_decode_noalloc(p: Problem, q, k_cache, v_cache, block_idx, out,
@@ -416,9 +428,12 @@ def decode_problem(x: dict, top_k: int) -> Problem:
 
 
 def decode(x: dict, top_k: int, out=None, block_scores=None, block_idx=None, workspace=None,
-           stream=None):
+           stream=None, topk: str = "separate"):
     """One MSA decode step: index scan -> top-k -> split-K sparse attention + combine.
+    topk="fused" selects inside the attention launch (msa_sparse_attn_decode_topk).
     Returns (out, block_idx, block_scores)."""
+    if topk not in ("separate", "fused"):
+        raise ValueError(f"topk must be 'separate' or 'fused', not {topk!r}")
     p = decode_problem(x, top_k)
     _check_out(out, "out", x["q"].shape, x["q"].dtype)
     _check_out(block_scores, "block_scores", (p.batch, p.num_groups, p.nblk), torch.float32)
@@ -432,6 +447,10 @@ def decode(x: dict, top_k: int, out=None, block_scores=None, block_idx=None, wor
     if workspace is None:
         workspace = alloc_workspace(p, "sparse_attn_decode", x["q"].device)
     msa_index_scores(p, x["q_idx"], x["k_idx"], block_scores, stream)
+    if topk == "fused":
+        msa_sparse_attn_decode_topk(p, x["q"], x["k_cache"], x["v_cache"], block_scores,
+                                    block_idx, out, workspace, stream)
+        return out, block_idx, block_scores
     msa_block_topk(p, block_scores, block_idx, stream)
     msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], block_idx, out, workspace,
                            stream)

@@ -41,7 +41,7 @@ KERNEL_SOURCES = {
     "decode_attn": "decode_attn.hip",
 }
 # device headers every kernel source includes: a change there can change any kernel
-SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h")
+SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h", "msa_select.h")
 
 
 def source_hash(kernel_name: str):

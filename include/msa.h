@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 #define MSA_BLOCK_SIZE 128
 #define MSA_HEAD_DIM 128
 #define MSA_MAX_TOPK 64
@@ -168,6 +168,25 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
 msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
                                   const void* v_cache, const int32_t* block_idx, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Index branch step 3 and the main branch, decode, in one call: the block selection of
+ * msa_block_topk (researchpapers.dev summary, "Mechanism": the local block plus the top_k - 1
+ * best earlier blocks, same ranking and layout) with msa_sparse_attn_decode (mlqm.cn blog,
+ * section 2.2: gather the kept blocks, then attention). block_scores is what
+ * msa_index_scores (decode) wrote, fp32 [B, G, ceil(max_len/128)]; the call writes block_idx
+ * (int32 [B, G, top_k]) with exactly the values msa_block_topk gives, and out bit for bit as
+ * msa_block_topk followed by msa_sparse_attn_decode. For bf16 rows of up to 1024 blocks, or
+ * up to 8192 blocks when B * G * top_k <= 2 * (the device's CU count), each attention
+ * workgroup selects its (sequence, group)'s blocks from the scores itself and takes the one
+ * of its slot, so the selection costs no launch of its own; otherwise the two kernels run
+ * one after the other. Workspace: msa_workspace_size(p, MSA_ENTRY_SPARSE_ATTN_DECODE) (else
+ * MSA_ERR_WORKSPACE_TOO_SMALL); mode must be MSA_MODE_DECODE (else MSA_ERR_INVALID_ARGUMENT).
+ */
+msa_status msa_sparse_attn_decode_topk(const msa_problem* p, const void* q, const void* k_cache,
+                                       const void* v_cache, const float* block_scores,
+                                       int32_t* block_idx, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * Allocation-free variant of msa_sparse_attn_decode, for callers that cannot allocate

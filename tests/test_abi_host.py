@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msa.load_library()
-    assert lib.msa_abi_version() == 3
+    assert lib.msa_abi_version() == 4
     for s in range(5):
         assert msa.status_string(s).startswith("MSA_")
 
@@ -329,3 +329,22 @@ def test_noalloc_decode_validation():
         msa.MSA_ERR_INVALID_ARGUMENT                                  # prefill problem
     assert call(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == msa.MSA_ERR_INVALID_ARGUMENT
     assert "scratch" in msa.status_string(msa.MSA_ERR_TOO_LARGE)
+
+
+def test_decode_topk_rejections():
+    """The decode attention with the selection folded in checks mode, alignment and the
+    workspace on the host, before any launch."""
+    lib = msa.load_library()
+    c = _decode()
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(c), msa.ENTRY["sparse_attn_decode"],
+                                  ctypes.byref(n)) == msa.MSA_OK and n.value > 0
+
+    def call(cp, ws=n.value, scores=FAKE, idx=FAKE):
+        return lib.msa_sparse_attn_decode_topk(ctypes.byref(cp), FAKE, FAKE, FAKE, scores, idx,
+                                               FAKE, FAKE, ws, 0)
+
+    assert call(_prefill().c()) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(c, scores=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(c, idx=FAKE + 8) == msa.MSA_ERR_INVALID_ARGUMENT
+    assert call(c, ws=n.value - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL

@@ -201,9 +201,17 @@ def test_prefill_pipeline_fused_index():
 
 
 def _run_decode(x, top_k):
+    """The decode step through msa_block_topk + msa_sparse_attn_decode and through
+    msa_sparse_attn_decode_topk (for bf16 the selection inside the attention launch), which
+    must give the same block ids and the same output bit for bit."""
     xd = _to(x)
     out, idx, bs = msa.decode(xd, top_k)
+    out_f = torch.full_like(out, 7.0)
+    idx_f = torch.full_like(idx, -7)
+    msa.decode(xd, top_k, out=out_f, block_idx=idx_f, topk="fused")
     torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx), "fused decode top-k: block ids differ"
+    assert torch.equal(out_f, out), "fused decode top-k: output differs"
     return parity.np32(out), idx.cpu().numpy(), parity.np32(bs)
 
 
@@ -376,6 +384,69 @@ def test_topk_long_rows_decode(nblk_max):
         for g in range(G):
             sel, _ = orc.select_blocks(s[b, g, :blocal].double().numpy(), blocal, top_k)
             assert got[b, g].tolist() == sel.tolist(), (b, g)
+
+
+def test_decode_topk_fused_crafted_scores():
+    """Crafted block-score rows through msa_sparse_attn_decode_topk: exact ties, -0.0/+0.0,
+    an all-equal row (every block a candidate: the heavily tied branch), winners in a short
+    tail, a row with fewer visible blocks than top_k, a one-token cache. Block ids against
+    the oracle's selection; output bit-identical to msa_block_topk + msa_sparse_attn_decode."""
+    G, Hpg, top_k, max_len = 2, 4, 16, 128 * 3000
+    lens = [max_len, 128 * 2049 + 5, 1300, 1]
+    B = len(lens)
+    nblk = max_len // 128
+    gen = torch.Generator().manual_seed(9)
+    s = torch.randn((B, G, nblk), generator=gen, dtype=torch.float32)
+    s[0, 0] = (torch.arange(nblk) % 5).float()                    # ties at the top value 4
+    s[0, 1] = 0.0
+    s[0, 1, 1::2] = -0.0
+    s[1, 0] = 1.0                                                  # all equal: overflow path
+    s[1, 0, 1000] = 3.0
+    s[1, 1, :2040] = -5.0                                          # winners in the short tail
+    gd = torch.Generator(device=DEV).manual_seed(10)
+    x = dict(q=torch.randn((B, G * Hpg, 128), generator=gd, device=DEV).bfloat16(),
+             k_cache=torch.randn((B, G, max_len, 128), generator=gd, device=DEV).bfloat16(),
+             v_cache=torch.randn((B, G, max_len, 128), generator=gd, device=DEV).bfloat16(),
+             q_idx=torch.zeros((B, G, 128), device=DEV, dtype=torch.bfloat16),
+             k_idx=torch.zeros((B, max_len, 128), device=DEV, dtype=torch.bfloat16),
+             seq_lens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+    p = msa.decode_problem(x, top_k)
+    sd = s.to(DEV)
+    ws = msa.alloc_workspace(p, "sparse_attn_decode")
+    idx_a = msa.alloc_block_idx(p)
+    out_a = torch.zeros_like(x["q"])
+    msa.msa_block_topk(p, sd, idx_a)
+    msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx_a, out_a, ws)
+    idx_b = torch.full_like(idx_a, -7)
+    out_b = torch.full_like(out_a, 7.0)
+    msa.msa_sparse_attn_decode_topk(p, x["q"], x["k_cache"], x["v_cache"], sd, idx_b, out_b, ws)
+    torch.cuda.synchronize()
+    got = idx_b.cpu().numpy()
+    for b in range(B):
+        blocal = (lens[b] - 1) // 128
+        for g in range(G):
+            sel, _ = orc.select_blocks(s[b, g, :blocal].double().numpy(), blocal, top_k)
+            assert got[b, g].tolist() == orc.selection_array([[sel]], top_k)[0, 0].tolist(), (b, g)
+    assert torch.equal(idx_a, idx_b) and torch.equal(out_a, out_b)
+
+
+@pytest.mark.parametrize("B,L,G,top_k", [
+    (4, 140000, 8, 16),   # 1094 blocks, 512 units: the selection inside the attention launch
+    (4, 140000, 9, 16),   # 576 units over 1024 blocks: the top-k kernel, then the attention
+])
+def test_decode_topk_fused_long_rows(B, L, G, top_k):
+    """msa_sparse_attn_decode_topk on rows longer than 1024 blocks, on both sides of its
+    choice between selecting inside the attention and the separate top-k kernel: the same
+    block ids and output as msa_block_topk + msa_sparse_attn_decode, bit for bit."""
+    x = synth.decode_inputs(B, L, G, 1, 128, 128, dtype="bf16", seed=B + G, planted_per_group=3,
+                            seq_lens=[L, L - 1000, 129 * 128, 4000], device=DEV)
+    print(f"fused decode top-k B={B} L={L} G={G} k={top_k}", flush=True)
+    out, idx, _ = msa.decode(x, top_k)
+    out_f = torch.full_like(out, 7.0)
+    idx_f = torch.full_like(idx, -7)
+    msa.decode(x, top_k, out=out_f, block_idx=idx_f, topk="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx) and torch.equal(out_f, out)
 
 
 def _sweep_prefill_cases(n=16, seed=2027):
