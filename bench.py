@@ -565,9 +565,8 @@ def run_decode(name, cfg, args, torch, msa, synth):
 
         def paged_step():
             msa.msa_index_scores_paged(p, x["q_idx"], pgd["k_idx_pages"], pgd["block_table"], bs)
-            msa.msa_block_topk(p, bs, pidx)
-            msa.msa_sparse_attn_decode_paged(p, x["q"], pgd["k_pages"], pgd["v_pages"],
-                                             pgd["block_table"], pidx, pout, ws)
+            msa.msa_sparse_attn_decode_topk_paged(p, x["q"], pgd["k_pages"], pgd["v_pages"],
+                                                  pgd["block_table"], bs, pidx, pout, ws)
         paged_ms = time_reps(torch, paged_step, args.steps)
         res["paged"] = dict(us_per_step=paged_ms * 1e3, us_per_token=paged_ms * 1e3 / B,
                             vs_contiguous=paged_ms / ms_plain,

@@ -197,6 +197,35 @@ msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q,
                                           p->heads_per_group, nsplit, st));
 }
 
+// msa_block_topk + the decode attention, or the attention workgroups selecting their own
+// blocks: when each of them reads a short row (<= 1024 blocks) or when every workgroup is
+// resident at once (one per (sequence, group, slot), two per CU). Otherwise the selection's
+// reads, repeated by every workgroup of a row, cost more than the top-k launch they save.
+msa_status run_decode_topk_attention(const msa_problem* p, const void* q, const void* k,
+                                     const void* v, const float* block_scores,
+                                     int32_t* block_idx, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t st, PageMap pm) {
+  if (!aligned16(block_scores) || !aligned16(block_idx) || !aligned16(out))
+    return MSA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < decode_ws_bytes(p, false)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t nblk = nblk_of(p);
+  const int64_t units = (int64_t)p->batch * p->num_groups * p->top_k;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MSA_ERR_HIP;
+  if (decode_block_kernel(p, false) && nblk <= kSelectMaxBlocks &&
+      (nblk <= 1024 || units <= 2 * (int64_t)cus))
+    return run_decode_attention(p, false, q, k, v, nullptr, out, workspace, workspace_bytes, st,
+                                pm, block_scores, block_idx);
+  hipError_t e = launch_block_topk(block_scores, block_idx, (int64_t)p->batch * p->num_groups,
+                                   p->num_groups, (int)nblk, p->top_k, 1, 0, p->seq_lens,
+                                   p->max_len, st);
+  if (e != hipSuccess) return MSA_ERR_HIP;
+  return run_decode_attention(p, false, q, k, v, block_idx, out, workspace, workspace_bytes, st,
+                              pm);
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,29 +419,9 @@ msa_status msa_sparse_attn_decode_topk(const msa_problem* p, const void* q, cons
   msa_status st = check_problem(p);
   if (st != MSA_OK) return st;
   if (p->mode != MSA_MODE_DECODE) return MSA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(block_scores) ||
-      !aligned16(block_idx) || !aligned16(out))
-    return MSA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < decode_ws_bytes(p, false)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-  // The attention workgroups select their own blocks when each of them reads a short row
-  // (<= 1024 blocks) or when every workgroup is resident at once (one per (sequence, group,
-  // slot), two per CU); otherwise the selection's reads, repeated by every workgroup of a
-  // row, cost more than the top-k launch they save.
-  const int64_t nblk = nblk_of(p);
-  const int64_t units = (int64_t)p->batch * p->num_groups * p->top_k;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return MSA_ERR_HIP;
-  if (decode_block_kernel(p, false) && nblk <= kSelectMaxBlocks &&
-      (nblk <= 1024 || units <= 2 * (int64_t)cus))
-    return run_decode_attention(p, false, q, k_cache, v_cache, nullptr, out, workspace,
-                                workspace_bytes, as_stream(stream), PageMap{}, block_scores,
-                                block_idx);
-  const msa_status s1 = msa_block_topk(p, block_scores, block_idx, stream);
-  if (s1 != MSA_OK) return s1;
-  return run_decode_attention(p, false, q, k_cache, v_cache, block_idx, out, workspace,
-                              workspace_bytes, as_stream(stream));
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return MSA_ERR_INVALID_ARGUMENT;
+  return run_decode_topk_attention(p, q, k_cache, v_cache, block_scores, block_idx, out,
+                                   workspace, workspace_bytes, as_stream(stream), PageMap{});
 }
 
 msa_status msa_sparse_attn_decode_noalloc(const msa_problem* p, const void* q,
@@ -476,6 +485,21 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, con
                    (int64_t)p->num_groups * MSA_BLOCK_SIZE * MSA_HEAD_DIM};
   return run_decode_attention(p, false, q, k_pages, v_pages, block_idx, out, workspace,
                               workspace_bytes, as_stream(stream), pm);
+}
+
+msa_status msa_sparse_attn_decode_topk_paged(const msa_problem* p, const void* q,
+                                             const void* k_pages, const void* v_pages,
+                                             const int32_t* block_table, int32_t pages_per_seq,
+                                             int64_t num_pages, const float* block_scores,
+                                             int32_t* block_idx, void* out, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  msa_status st = check_paged(p, block_table, pages_per_seq, num_pages);
+  if (st != MSA_OK) return st;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages)) return MSA_ERR_INVALID_ARGUMENT;
+  const PageMap pm{block_table, pages_per_seq, num_pages,
+                   (int64_t)p->num_groups * MSA_BLOCK_SIZE * MSA_HEAD_DIM};
+  return run_decode_topk_attention(p, q, k_pages, v_pages, block_scores, block_idx, out,
+                                   workspace, workspace_bytes, as_stream(stream), pm);
 }
 
 msa_status msa_dense_gqa_attn(const msa_problem* p, const void* q, const void* k, const void* v,

@@ -37,6 +37,7 @@ BLOCK = 128
 EXPORTED = ["msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
             "msa_sparse_attn_decode", "msa_sparse_attn_decode_topk",
             "msa_sparse_attn_decode_noalloc", "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
+            "msa_sparse_attn_decode_topk_paged",
             "msa_index_kl_prefill", "msa_dense_gqa_attn", "msa_workspace_size",
             "msa_status_string", "msa_abi_version"]
 
@@ -83,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.msa_index_scores_paged.argtypes = [pp, vp, vp, vp, i32, i64, vp, vp]
     lib.msa_sparse_attn_decode_paged.argtypes = [pp, vp, vp, vp, vp, i32, i64, vp, vp, vp, sz, vp]
+    lib.msa_sparse_attn_decode_topk_paged.argtypes = [pp, vp, vp, vp, vp, i32, i64, vp, vp, vp,
+                                                      vp, sz, vp]
     lib.msa_index_kl_prefill.argtypes = [pp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                          vp, sz, vp]
     lib.msa_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(sz)]
@@ -91,7 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_abi_version.argtypes = []
     for name in ("msa_index_scores", "msa_block_topk", "msa_index_topk", "msa_sparse_attn_prefill",
                  "msa_index_scores_paged", "msa_sparse_attn_decode_paged",
-                 "msa_sparse_attn_decode", "msa_sparse_attn_decode_topk",
+                 "msa_sparse_attn_decode_topk_paged", "msa_sparse_attn_decode", "msa_sparse_attn_decode_topk",
                  "msa_sparse_attn_decode_noalloc", "msa_dense_gqa_attn", "msa_workspace_size",
                  "msa_index_kl_prefill",
                  "msa_abi_version"):
@@ -209,6 +212,16 @@ def msa_sparse_attn_decode_paged(p: Problem, q, k_pages, v_pages, block_table, b
         ctypes.byref(p.c()), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
         int(block_table.shape[1]), int(k_pages.shape[0]), _ptr(block_idx), _ptr(out),
         _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode_paged")
+
+
+def msa_sparse_attn_decode_topk_paged(p: Problem, q, k_pages, v_pages, block_table, block_scores,
+                                      block_idx, out, workspace=None, stream=None):
+    """msa_sparse_attn_decode_topk on paged caches (see include/msa.h)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().msa_sparse_attn_decode_topk_paged(
+        ctypes.byref(p.c()), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+        int(block_table.shape[1]), int(k_pages.shape[0]), _ptr(block_scores), _ptr(block_idx),
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)), "msa_sparse_attn_decode_topk_paged")
 
 
 def index_topk_supported(p: Problem) -> bool:

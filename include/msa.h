@@ -234,6 +234,14 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q, con
                                         int32_t pages_per_seq, int64_t num_pages,
                                         const int32_t* block_idx, void* out, void* workspace,
                                         size_t workspace_bytes, void* stream);
+/* msa_sparse_attn_decode_topk on the paged caches above (same arguments as
+ * msa_sparse_attn_decode_paged, with block_scores in, block_idx out). */
+msa_status msa_sparse_attn_decode_topk_paged(const msa_problem* p, const void* q,
+                                             const void* k_pages, const void* v_pages,
+                                             const int32_t* block_table, int32_t pages_per_seq,
+                                             int64_t num_pages, const float* block_scores,
+                                             int32_t* block_idx, void* out, void* workspace,
+                                             size_t workspace_bytes, void* stream);
 
 /*
  * Index-branch KL loss and its gradient, prefill (the training side of the index branch:

@@ -346,5 +346,12 @@ def test_decode_topk_rejections():
 
     assert call(_prefill().c()) == msa.MSA_ERR_INVALID_ARGUMENT
     assert call(c, scores=FAKE + 4) == msa.MSA_ERR_INVALID_ARGUMENT
+    cp = _decode(max_len=4096)
+    assert lib.msa_sparse_attn_decode_topk_paged(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 31, 100,
+                                                 FAKE, FAKE, FAKE, FAKE, n.value, 0) \
+        == msa.MSA_ERR_INVALID_ARGUMENT  # max_len != pages_per_seq * 128
+    assert lib.msa_sparse_attn_decode_topk_paged(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 32, 100,
+                                                 FAKE, FAKE, FAKE, FAKE, 0, 0) \
+        == msa.MSA_ERR_WORKSPACE_TOO_SMALL
     assert call(c, idx=FAKE + 8) == msa.MSA_ERR_INVALID_ARGUMENT
     assert call(c, ws=n.value - 1) == msa.MSA_ERR_WORKSPACE_TOO_SMALL

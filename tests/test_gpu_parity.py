@@ -291,6 +291,14 @@ def test_paged_decode_equals_contiguous(B, L, G, Hpg, d_idx, top_k, dtype, lens)
         outs.append((bs, idx, out))
     (bs1, idx1, out1), (bs2, idx2, out2) = outs
     assert torch.equal(bs1, bs2) and torch.equal(idx1, idx2) and torch.equal(out1, out2)
+    # the paged entry with the selection folded in: the same ids and output
+    idx3 = torch.full_like(idx2, -7)
+    out3 = torch.full_like(out2, 7.0)
+    msa.msa_sparse_attn_decode_topk_paged(p, xd["q"], pg["k_pages"], pg["v_pages"],
+                                          pg["block_table"], bs2, idx3, out3,
+                                          msa.alloc_workspace(p, "sparse_attn_decode"))
+    torch.cuda.synchronize()
+    assert torch.equal(idx3, idx2) and torch.equal(out3, out2)
     res = orc.decode(x["q"], x["k_cache"], x["v_cache"], x["q_idx"], x["k_idx"], x["seq_lens"],
                      top_k)
     parity.check_decode(x, parity.np32(out2), idx2.cpu().numpy(), parity.np32(bs2), res, top_k,
