@@ -123,10 +123,10 @@ __global__ __launch_bounds__(256, 2) void kl_stats_unit_kernel(
       float mx = -INFINITY;
       int lq = limq;
       asm volatile("" : "+v"(lq));
+      if (main) s_tiles4_swz(Kb, n32, qop, q, sv);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        sv[kt] = main ? s_tile_swz(Kb, 32 * kt + n32, qop, q)
-                      : s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
+        if (!main) sv[kt] = s_tile_vswz(KIb, 32 * kt + n32, qiop, q);
         if (cut) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -246,9 +246,11 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
       // kept as 64 hoisted lane masks, which the compiler would spill
       int lq = limq;
       asm volatile("" : "+v"(lq));
+      f32x16 acc4[4];
+      s_tiles4_swz(Kb, n32, qop, q, acc4);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const f32x16 sv = s_tile_swz(Kb, 32 * kt + n32, qop, q);
+        const f32x16 sv = acc4[kt];
         if (cut) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
