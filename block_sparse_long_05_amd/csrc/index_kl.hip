@@ -226,7 +226,6 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
     const int lim = min(max((int)t - c * kBlock, -1), kBlock - 1);
     const int limq = ok ? lim - 4 * q : -1024;  // no key is visible to a lane without entry
     const uint16_t* qrow = Q + (t * Hq + (int64_t)g * Hpg) * kHeadDim;
-    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q);
     const float* lrow = lse + rowg * (Hpg + 1);
     float w[4][16];
 #pragma unroll
@@ -278,6 +277,7 @@ __global__ __launch_bounds__(512, 2) void kl_grad_unit_kernel(
         head_p(qb, lb);
       }
     }
+    load_row_op(qiop, QI + (t * G + g) * kHeadDim, q);
     const float inv_h = 1.f / (float)Hpg;
     const float li = lrow[Hpg];
     float lsum = 0.f;
