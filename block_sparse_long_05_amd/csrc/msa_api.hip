@@ -138,6 +138,24 @@ msa_status device_scratch(void** out) {
   return MSA_OK;
 }
 
+// Compute units of the current device (queried on the device's first call, then cached).
+std::atomic<int> g_cu_count[kMaxDevices];
+
+msa_status device_cu_count(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MSA_ERR_UNSUPPORTED;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return MSA_ERR_HIP;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return MSA_OK;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 msa_status run_decode_attention(const msa_problem* p, bool dense, const void* q, const void* k,
@@ -210,10 +228,9 @@ msa_status run_decode_topk_attention(const msa_problem* p, const void* q, const 
   if (workspace_bytes < decode_ws_bytes(p, false)) return MSA_ERR_WORKSPACE_TOO_SMALL;
   const int64_t nblk = nblk_of(p);
   const int64_t units = (int64_t)p->batch * p->num_groups * p->top_k;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return MSA_ERR_HIP;
+  int cus = 0;
+  const msa_status sc = device_cu_count(&cus);
+  if (sc != MSA_OK) return sc;
   if (decode_block_kernel(p, false) && nblk <= kSelectMaxBlocks &&
       (nblk <= 1024 || units <= 2 * (int64_t)cus))
     return run_decode_attention(p, false, q, k, v, nullptr, out, workspace, workspace_bytes, st,
