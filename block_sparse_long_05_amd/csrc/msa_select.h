@@ -13,7 +13,8 @@
 //      each hold a distinct key >= LB), or of the 256 thread maxima when K > 16 (a tighter
 //      bound keeps the candidates few), and at least 1 so that padding keys (0) never pass;
 //   3. each wave writes its keys >= LB to its own LDS region as 64-bit values
-//      (key << 32) | ~block, which are distinct and order the row exactly by the rule;
+//      (key << 32) | ~block, which are distinct and order the row exactly by the rule (when
+//      ties make those many, the keys > LB and only its K lowest-id keys == LB);
 //   4. one wave keeps the K largest of those values (up to 256 candidates: each is kept
 //      when fewer than K others are larger; more, in heavily tied rows: the K-th largest
 //      from a most-significant-bit-first search).
@@ -101,16 +102,69 @@ __device__ __forceinline__ void row_select_wg(const float* __restrict__ s, bool 
   lb = max(lb, 1u);  // padding keys (0) never pass
   // this wave's candidates, in its own region of cand
   uint64_t* cw = cand + wave * kWaveCand;
+  auto cval = [&](int j) {
+    return ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk(j));
+  };
   int n = 0;
 #pragma unroll
   for (int j = 0; j < kRowPer; ++j) {
     const bool take = key[j] >= lb;
     const uint64_t m = __ballot(take);
     if (m == 0) continue;
-    if (take)
-      cw[n + __popcll(m & lanemask_lt(lane))] =
-          ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)blk(j));
+    if (take) cw[n + __popcll(m & lanemask_lt(lane))] = cval(j);
     n += __popcll(m);
+  }
+  if (n > 64) {
+    n = 0;  // the region is written again
+    // Many keys at or above the bound, i.e. ties at it (an all-equal row: every key). Keys
+    // above the bound all go; of the keys equal to it the row can keep only the K with the
+    // lowest block ids, and those are among the K lowest of their own wave, so the wave offers
+    // just those: ranked by block id, i.e. by (slab, lane, position) for 16-byte rows and by
+    // (j, lane) otherwise.
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const bool take = key[j] > lb;
+      const uint64_t m = __ballot(take);
+      if (m == 0) continue;
+      if (take) cw[n + __popcll(m & lanemask_lt(lane))] = cval(j);
+      n += __popcll(m);
+    }
+    int r0 = 0;  // the wave's equal keys in lower ids
+    if (vec) {
+#pragma unroll
+      for (int j4 = 0; j4 < kRowPer / 4; ++j4) {
+        if (r0 >= K) break;
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt += key[4 * j4 + i] == lb ? 1 : 0;
+        int incl = cnt;  // inclusive prefix over the wave's lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += y;
+        }
+        int r = r0 + incl - cnt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (key[4 * j4 + i] == lb) {
+            if (r < K) cw[n + r] = cval(4 * j4 + i);
+            ++r;
+          }
+        }
+        r0 += __shfl(incl, 63, 64);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kRowPer; ++j) {
+        if (r0 >= K) break;
+        const bool eq = key[j] == lb;
+        const uint64_t m = __ballot(eq);
+        const int r = r0 + __popcll(m & lanemask_lt(lane));
+        if (eq && r < K) cw[n + r] = cval(j);
+        r0 += __popcll(m);
+      }
+    }
+    n += min(r0, K);
   }
   if (lane == 0) sh.wcount[wave] = n;
   __syncthreads();
