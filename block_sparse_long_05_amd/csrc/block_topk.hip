@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
       const uint32_t cand = lb | (1u << bit);
       if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
     }
-    // b > K valid blocks sit in at least K lanes, so LB > 0 and padding keys never pass
+    lb = max(lb, 1u);  // padding keys (0) never pass
     int n = 0;
 #pragma unroll
     for (int j = 0; j < kWaveHeld; ++j) {
@@ -187,6 +187,65 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
         ci[pos] = blk(j);
       }
       n += __popcll(m);
+    }
+    if (n > 128) {
+      // Ties at the bound (an all-equal row: every key). Keys above it all go; of the keys
+      // equal to it the row keeps at most the K with the lowest ids, so only those are
+      // offered, ranked by block id: (slab, lane, position) for 16-byte rows, else (j, lane).
+      n = 0;
+#pragma unroll
+      for (int j = 0; j < kWaveHeld; ++j) {
+        const bool take = key[j] > lb;
+        const uint64_t m = __ballot(take);
+        const int pos = n + __popcll(m & lanemask_lt(lane));
+        if (take && pos < kCandCap) {
+          ck[pos] = key[j];
+          ci[pos] = blk(j);
+        }
+        n += __popcll(m);
+      }
+      int r0 = 0;  // equal keys in lower ids
+      if (vec) {
+#pragma unroll
+        for (int j4 = 0; j4 < kWaveHeld / 4; ++j4) {
+          if (r0 >= K) break;
+          int cnt = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cnt += key[4 * j4 + i] == lb ? 1 : 0;
+          int incl = cnt;  // inclusive prefix over the lanes
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+          }
+          int r = r0 + incl - cnt;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (key[4 * j4 + i] == lb) {
+              if (r < K && n + r < kCandCap) {
+                ck[n + r] = lb;
+                ci[n + r] = blk(4 * j4 + i);
+              }
+              ++r;
+            }
+          }
+          r0 += __shfl(incl, 63, 64);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kWaveHeld; ++j) {
+          if (r0 >= K) break;
+          const bool eq = key[j] == lb;
+          const uint64_t m = __ballot(eq);
+          const int r = r0 + __popcll(m & lanemask_lt(lane));
+          if (eq && r < K && n + r < kCandCap) {
+            ck[n + r] = lb;
+            ci[n + r] = blk(j);
+          }
+          r0 += __popcll(m);
+        }
+      }
+      n += min(r0, K);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -227,13 +286,18 @@ __global__ __launch_bounds__(64 * kTopkWaves) void block_topk_kernel(
     const uint32_t cand = lb | (1u << bit);
     if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
   }
-  // 2. compact the candidates (ascending block order).
-  int n = 0;
+  lb = max(lb, 1u);
+  // 2. compact the candidates (ascending block order): every key above the bound, and of the
+  //    keys equal to it only the first K (the row keeps at most the K lowest-id ones of those)
+  int n = 0, neq = 0;
   for (int c0 = 0; c0 < b; c0 += 64) {
     const int c = c0 + lane;
     uint32_t key = 0;
     if (c < b) key = ordered_key(s[c]);
-    const bool take = c < b && key >= lb;
+    const bool eq = c < b && key == lb;
+    const uint64_t me = __ballot(eq);
+    const bool take = (c < b && key > lb) || (eq && neq + __popcll(me & lanemask_lt(lane)) < K);
+    neq += __popcll(me);
     const uint64_t m = __ballot(take);
     const int pos = n + __popcll(m & lanemask_lt(lane));
     if (take && pos < kCandCap) {
@@ -323,14 +387,21 @@ __global__ __launch_bounds__(64 * kLongWaves) void block_topk_long_kernel(
       const uint32_t cand = lb | (1u << bit);
       if ((int)__popcll(__ballot(lmax >= cand)) >= K) lb = cand;
     }
+    lb = max(lb, 1u);
     uint32_t* ck = seg_key[wave];
     int32_t* ci = seg_idx[wave];
-    int nc = 0;
+    // every key above the bound; of the keys equal to it only the first K in block order (the
+    // segment keeps at most the K lowest-id ones of those)
+    int nc = 0, neq = 0;
     if (in_regs) {
 #pragma unroll
       for (int j = 0; j < kHeld; ++j) {
         const int c = lo + 64 * j + lane;
-        const bool take = c < hi && held[j] >= lb;
+        const bool eq = c < hi && held[j] == lb;
+        const uint64_t me = __ballot(eq);
+        const bool take =
+            (c < hi && held[j] > lb) || (eq && neq + __popcll(me & lanemask_lt(lane)) < K);
+        neq += __popcll(me);
         const uint64_t m = __ballot(take);
         const int pos = nc + __popcll(m & lanemask_lt(lane));
         if (take && pos < kCandCap) {
@@ -344,7 +415,10 @@ __global__ __launch_bounds__(64 * kLongWaves) void block_topk_long_kernel(
         const int c = c0 + lane;
         uint32_t key = 0;
         if (c < hi) key = ordered_key(s[c]);
-        const bool take = c < hi && key >= lb;
+        const bool eq = c < hi && key == lb;
+        const uint64_t me = __ballot(eq);
+        const bool take = (c < hi && key > lb) || (eq && neq + __popcll(me & lanemask_lt(lane)) < K);
+        neq += __popcll(me);
         const uint64_t m = __ballot(take);
         const int pos = nc + __popcll(m & lanemask_lt(lane));
         if (take && pos < kCandCap) {

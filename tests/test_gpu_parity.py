@@ -340,25 +340,30 @@ def test_repeat_runs_bit_identical():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_topk_handles_ties_and_minus_zero_on_device():
+@pytest.mark.parametrize("nb,top_k", [(700, 4), (700, 16), (3000, 16), (3001, 40)])
+def test_topk_handles_ties_and_minus_zero_on_device(nb, top_k):
     """Crafted block-score rows through msa_block_topk (no index kernel): exact ties,
-    -0.0 vs +0.0, a row whose candidates overflow the LDS buffer (all equal)."""
-    G, top_k, T = 1, 4, 128 * 700
+    -0.0 vs +0.0, all-equal rows (every block tied: only the lowest ids may be offered as
+    candidates), on rows held in registers (<= 2048 blocks) and longer ones, 16-byte aligned
+    rows and others."""
+    G, T = 1, 128 * nb
     p = msa.Problem(dtype="bf16", mode="prefill", num_groups=G, heads_per_group=1, index_dim=128,
-                    top_k=top_k, seq_len=T, q_begin=T - 3, q_count=3)
+                    top_k=top_k, seq_len=T, q_begin=T - 4, q_count=4)
     nblk = p.nblk
     b = (T - 1) // 128
-    s = torch.zeros((3, G, nblk), dtype=torch.float32)
+    s = torch.zeros((4, G, nblk), dtype=torch.float32)
     s[0, 0, :b] = torch.arange(b, dtype=torch.float32) % 7       # many exact ties at 6
     s[1, 0, :b] = 0.0
     s[1, 0, 1:b:2] = -0.0                                           # all zero: lowest ids win
-    s[2, 0, :b] = 1.0                                               # all equal: overflow path
-    s[2, 0, 650] = 2.0
-    idx = torch.empty((3, G, top_k), dtype=torch.int32, device=DEV)
+    s[2, 0, :b] = 1.0                                               # all equal but one
+    s[2, 0, b // 2 + 3] = 2.0
+    s[3, 0, :b] = 1.0
+    s[3, 0, b - 20:b] = 1.5                                         # 20 winners at the end
+    idx = torch.empty((4, G, top_k), dtype=torch.int32, device=DEV)
     msa.msa_block_topk(p, s.to(DEV), idx)
     torch.cuda.synchronize()
     got = idx.cpu().numpy()
-    for r in range(3):
+    for r in range(4):
         sel, _ = orc.select_blocks(s[r, 0, :b].double().numpy(), b, top_k)
         assert got[r, 0].tolist() == sel.tolist(), r
 
