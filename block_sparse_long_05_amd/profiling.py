@@ -26,22 +26,22 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# kernel-name fragment -> source file that defines it
+# kernel-name fragment -> source files that define it (beyond the shared headers)
 KERNEL_SOURCES = {
-    "index_scores_prefill": "index_scores.hip",
-    "index_scores_decode": "index_scores.hip",
-    "index_topk": "index_scores.hip",
-    "block_topk": "block_topk.hip",
-    "kv_": "attn_tile.hip",
-    "qtile_attn": "attn_tile.hip",
-    "dense_attn": "attn_tile.hip",
-    "gather_attn": "attn_gather.hip",
-    "decode_combine": "attn_gather.hip",
-    "kl_": "index_kl.hip",
-    "decode_attn": "decode_attn.hip",
+    "index_scores_prefill": ("index_scores.hip",),
+    "index_scores_decode": ("index_scores.hip",),
+    "index_topk": ("index_scores.hip",),
+    "block_topk": ("block_topk.hip", "msa_select.h"),
+    "kv_": ("attn_tile.hip",),
+    "qtile_attn": ("attn_tile.hip",),
+    "dense_attn": ("attn_tile.hip",),
+    "gather_attn": ("attn_gather.hip",),
+    "decode_combine": ("attn_gather.hip",),
+    "kl_": ("index_kl.hip",),
+    "decode_attn": ("decode_attn.hip", "msa_select.h"),
 }
 # device headers every kernel source includes: a change there can change any kernel
-SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h", "msa_select.h")
+SHARED_HEADERS = ("msa_device.h", "msa_tile.h", "msa_launch.h")
 
 
 def source_hash(kernel_name: str):
@@ -50,7 +50,7 @@ def source_hash(kernel_name: str):
     for frag, src in KERNEL_SOURCES.items():
         if frag in kernel_name:
             h = hashlib.sha256()
-            for f in (src,) + SHARED_HEADERS:
+            for f in src + SHARED_HEADERS:
                 path = os.path.join(CSRC, f)
                 if os.path.exists(path):
                     h.update(open(path, "rb").read())
