@@ -228,6 +228,7 @@ DECODE_CASES = [
     (2, 2500, [2500, 1000], 2, 3, 128, 4, "f32", 0),     # fp32 with index dim 128
     (3, 2000, [2000, 129, 1], 4, 8, 128, 1, "bf16", 0),  # top_k 1: only the local block
     (2, 1500, [1500, 700], 2, 3, 64, 1, "f32", 0),       # top_k 1, fp32
+    (2, 3000, [3000, 1700], 64, 1, 128, 4, "bf16", 1),   # the most groups the ABI allows
 ]
 
 
