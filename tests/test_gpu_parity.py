@@ -444,6 +444,47 @@ def test_decode_topk_fused_crafted_scores():
     assert torch.equal(idx_a, idx_b) and torch.equal(out_a, out_b)
 
 
+@pytest.mark.parametrize("top_k", [64, 17])
+def test_decode_topk_fused_tied_long_rows(top_k):
+    """Rows of 8192 blocks with every score tied (and one with ties above the bound) through
+    msa_block_topk and msa_sparse_attn_decode_topk (selection inside the attention: 2 x 2 x
+    top_k workgroups): the lowest ids win, both entries agree bit for bit. top_k 64 takes the
+    lower bound from the 256 thread maxima, top_k 17 from the 64 group maxima."""
+    B, G, Hpg, max_len = 2, 2, 2, 128 * 8192
+    nblk = max_len // 128
+    s = torch.zeros((B, G, nblk), dtype=torch.float32)              # all tied (zero queries)
+    s[0, 1] = 1.0
+    s[0, 1, 4000:4100] = 2.0                                        # 100 tied winners above
+    s[1, 0] = -0.0
+    s[1, 1] = 3.0
+    lens = [max_len, max_len - 77]
+    gd = torch.Generator(device=DEV).manual_seed(12)
+    x = dict(q=torch.randn((B, G * Hpg, 128), generator=gd, device=DEV).bfloat16(),
+             k_cache=torch.randn((B, G, max_len, 128), generator=gd, device=DEV).bfloat16(),
+             v_cache=torch.randn((B, G, max_len, 128), generator=gd, device=DEV).bfloat16(),
+             q_idx=torch.zeros((B, G, 128), device=DEV, dtype=torch.bfloat16),
+             k_idx=torch.zeros((B, max_len, 128), device=DEV, dtype=torch.bfloat16),
+             seq_lens=torch.tensor(lens, dtype=torch.int32, device=DEV))
+    p = msa.decode_problem(x, top_k)
+    sd = s.to(DEV)
+    ws = msa.alloc_workspace(p, "sparse_attn_decode")
+    idx_a = msa.alloc_block_idx(p)
+    out_a = torch.zeros_like(x["q"])
+    msa.msa_block_topk(p, sd, idx_a)
+    msa.msa_sparse_attn_decode(p, x["q"], x["k_cache"], x["v_cache"], idx_a, out_a, ws)
+    idx_b = torch.full_like(idx_a, -7)
+    out_b = torch.full_like(out_a, 7.0)
+    msa.msa_sparse_attn_decode_topk(p, x["q"], x["k_cache"], x["v_cache"], sd, idx_b, out_b, ws)
+    torch.cuda.synchronize()
+    got = idx_a.cpu().numpy()
+    for b in range(B):
+        blocal = (lens[b] - 1) // 128
+        for g in range(G):
+            sel, _ = orc.select_blocks(s[b, g, :blocal].double().numpy(), blocal, top_k)
+            assert got[b, g].tolist() == orc.selection_array([[sel]], top_k)[0, 0].tolist(), (b, g)
+    assert torch.equal(idx_a, idx_b) and torch.equal(out_a, out_b)
+
+
 @pytest.mark.parametrize("B,L,G,top_k", [
     (4, 140000, 8, 16),   # 1094 blocks, 512 units: the selection inside the attention launch
     (4, 140000, 9, 16),   # 576 units over 1024 blocks: the top-k kernel, then the attention
